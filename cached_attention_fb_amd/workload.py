@@ -1,0 +1,207 @@
+"""Seeded synthetic inputs for the block-diffusion attention step.
+
+This module only draws random numbers and rounds them to the working dtype.
+It holds none of the attention arithmetic, so both the HIP path and the
+float64 CPU checker consume exactly the same values from it.
+
+What is drawn follows the setting of FlashBlock (page "Résumé Technique :
+FlashBlock", §1 and §2): a prefix KV cache of committed tokens, and a current
+block whose queries/keys/values change from one denoising step to the next.
+
+* dLLM workloads: at every step after the first, ``M`` block positions per
+  sequence are chosen uniformly without replacement and the Q, K and V rows of
+  those positions (all heads) are redrawn.  ``M`` is what the threshold policy
+  compares with tau (§2 "Stratégies de Réutilisation Adaptatives").
+* video workload: block K/V stay fixed; at every step (the first included)
+  all block queries are ``Q_base + sigma_h * eps`` with fresh iid ``eps`` and
+  one ``sigma_h ~ U(0.01, 0.5)`` per head, drawn once per block.
+
+Draw order for one generator ``numpy.random.default_rng(seed)``: prefix K,
+prefix V; then per block: block Q, K, V; (video) sigma; then per step: M,
+positions, redrawn rows (or eps).  Values are drawn in float64 and rounded
+once to the working dtype (bf16 with torch's round-to-nearest-even cast,
+fp32 with numpy's).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape, value distribution and reuse policy of one synthetic workload."""
+
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    prefix: int          # committed prefix tokens at the first block
+    block: int           # tokens per block (Bs)
+    steps: int           # denoising steps per block (S)
+    blocks: int          # blocks generated in a row (prefix grows by Bs each)
+    dtype: str           # "f32" | "bf16"
+    value_std: float     # standard deviation of every drawn element
+    update: str          # "uniform" | "binomial" | "video"
+    update_a: float      # uniform: max M; binomial: n; video: sigma low
+    update_b: float      # binomial: p; video: sigma high
+    policy: str          # "tau" | "gamma"
+    tau: int = 0
+    gamma: float = 0.0
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def max_prefix(self) -> int:
+        return self.prefix + self.block * (self.blocks - 1)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def with_(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+_S128 = 1.0 / math.sqrt(128.0)
+
+WORKLOADS = {
+    "tiny-fp32": Workload(
+        name="tiny-fp32", batch=1, n_q_heads=4, n_kv_heads=4, head_dim=64,
+        prefix=512, block=32, steps=8, blocks=2, dtype="f32", value_std=1.0,
+        update="uniform", update_a=8, update_b=0, policy="tau", tau=4, seed=1100,
+        description="1 sequence, 4 heads MHA, D=64, prefix 512, block 32, 8 steps, fp32"),
+    "dllm-8k": Workload(
+        name="dllm-8k", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        prefix=8192, block=32, steps=8, blocks=1, dtype="bf16", value_std=_S128,
+        update="binomial", update_a=32, update_b=0.15, policy="tau", tau=8, seed=1200,
+        description="batch 1, 32/8 heads (GQA 4), D=128, prefix 8192, block 32, 8 steps, bf16"),
+    "long-32k-b4": Workload(
+        name="long-32k-b4", batch=4, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        prefix=32768, block=32, steps=16, blocks=1, dtype="bf16", value_std=_S128,
+        update="binomial", update_a=32, update_b=0.15, policy="tau", tau=8, seed=1300,
+        description="batch 4, 32/8 heads, D=128, prefix 32768, block 32, 16 steps, bf16"),
+    "video-1560x15600": Workload(
+        name="video-1560x15600", batch=1, n_q_heads=12, n_kv_heads=12, head_dim=128,
+        prefix=15600, block=1560, steps=4, blocks=1, dtype="bf16", value_std=1.0,
+        update="video", update_a=0.01, update_b=0.5, policy="gamma", gamma=0.95,
+        seed=1400,  # replaced by the first seed passing the margin rule, see VIDEO_SEED
+        description="batch 1, 12 heads MHA, D=128, frame block 30x52=1560, prefix 10 frames, 4 steps, bf16"),
+    "max-128k": Workload(
+        name="max-128k", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        prefix=131072, block=64, steps=8, blocks=1, dtype="bf16", value_std=_S128,
+        update="binomial", update_a=64, update_b=0.1, policy="tau", tau=16, seed=1500,
+        description="batch 1, 32/8 heads, D=128, prefix 131072, block 64, 8 steps, bf16"),
+}
+
+# First seed >= 1400 whose float64 run keeps every cosine-similarity decision
+# more than 1e-3 away from gamma; written by tests/golden/make_video_seed.py.
+VIDEO_SEED = 1400
+
+
+def workload(name: str) -> Workload:
+    w = WORKLOADS[name]
+    if w.update == "video":
+        w = w.with_(seed=VIDEO_SEED)
+    return w
+
+
+@dataclass
+class StepInputs:
+    q: torch.Tensor               # [B, Hq, Bs, D] working dtype, CPU
+    k: torch.Tensor               # [B, Hkv, Bs, D]
+    v: torch.Tensor               # [B, Hkv, Bs, D]
+    n_updated: np.ndarray         # int32 [B]: block tokens redrawn at this step
+
+
+@dataclass
+class BlockInputs:
+    steps: List[StepInputs] = field(default_factory=list)
+    sigma: Optional[np.ndarray] = None   # video: per-head perturbation scale
+
+
+@dataclass
+class Inputs:
+    workload: Workload
+    seed: int
+    k_prefix: torch.Tensor        # [B, Hkv, prefix, D] working dtype, CPU
+    v_prefix: torch.Tensor
+    blocks: List[BlockInputs]
+
+
+def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+
+
+def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    x = rng.standard_normal(shape)
+    if std != 1.0:
+        x *= std
+    return x
+
+
+def generate(w: Workload, seed: Optional[int] = None, prefix: Optional[int] = None) -> Inputs:
+    """Draw every input of ``w.blocks`` blocks of ``w.steps`` steps.
+
+    ``prefix`` overrides the workload's prefix length (tests use it to build
+    small and ragged cases with the same distributions)."""
+    seed = w.seed if seed is None else seed
+    n_pre = w.prefix if prefix is None else prefix
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, D, Bs = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block
+    k_pre = _round(_normal(rng, (B, Hkv, n_pre, D), w.value_std), w.dtype)
+    v_pre = _round(_normal(rng, (B, Hkv, n_pre, D), w.value_std), w.dtype)
+    blocks = []
+    for _ in range(w.blocks):
+        q = _normal(rng, (B, Hq, Bs, D), w.value_std)
+        k = _normal(rng, (B, Hkv, Bs, D), w.value_std)
+        v = _normal(rng, (B, Hkv, Bs, D), w.value_std)
+        blk = BlockInputs()
+        if w.update == "video":
+            blk.sigma = rng.uniform(w.update_a, w.update_b, size=Hq)
+            k_r, v_r = _round(k, w.dtype), _round(v, w.dtype)
+            for _s in range(w.steps):
+                eps = rng.standard_normal((B, Hq, Bs, D))
+                q_s = q + blk.sigma[None, :, None, None] * eps
+                blk.steps.append(StepInputs(_round(q_s, w.dtype), k_r, v_r,
+                                            np.full(B, Bs, dtype=np.int32)))
+        else:
+            for s in range(w.steps):
+                m = np.zeros(B, dtype=np.int32)
+                if s > 0:
+                    for b in range(B):
+                        if w.update == "uniform":
+                            m[b] = rng.integers(0, int(w.update_a) + 1)
+                        else:
+                            m[b] = rng.binomial(int(w.update_a), w.update_b)
+                        pos = rng.choice(Bs, size=int(m[b]), replace=False)
+                        if m[b]:
+                            q[b][:, pos, :] = _normal(rng, (Hq, int(m[b]), D), w.value_std)
+                            k[b][:, pos, :] = _normal(rng, (Hkv, int(m[b]), D), w.value_std)
+                            v[b][:, pos, :] = _normal(rng, (Hkv, int(m[b]), D), w.value_std)
+                blk.steps.append(StepInputs(_round(q, w.dtype), _round(k, w.dtype),
+                                            _round(v, w.dtype), m))
+        blocks.append(blk)
+    return Inputs(w, seed, k_pre, v_pre, blocks)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of a working-dtype tensor to a float64 numpy array."""
+    return t.to(torch.float64).numpy()

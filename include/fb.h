@@ -1,0 +1,185 @@
+/*
+ * fb.h -- C ABI of the FlashBlock attention-step library (libfb.so, gfx950).
+ *
+ * FlashBlock ("FlashBlock: Attention Caching for Efficient Long-Context Block
+ * Diffusion", page "Résumé Technique : FlashBlock", §2 "Mécanisme Central")
+ * splits the attention of a denoising step of block diffusion into
+ *   - block-external attention A_out over the tokens outside the current
+ *     block (the committed prefix KV cache), with its log-normaliser
+ *     L_out = log Z_out, which are cached and may be reused by later steps;
+ *   - block-internal attention A_in, L_in over the block's own tokens;
+ *   - the log-space merge A_full = (e^{L_out-m} A_out + e^{L_in-m} A_in) /
+ *     (e^{L_out-m} + e^{L_in-m}) with m = max(L_out, L_in).
+ * A step reuses the cache when the number M of updated block tokens is below
+ * a threshold tau, or, per head, when the head's similarity across steps
+ * exceeds gamma (§2 "Stratégies de Réutilisation Adaptatives").
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns fb_status; FB_OK is 0.  No C++ exception crosses the
+ *     ABI.  On an error, fb_last_error() holds a message for the calling
+ *     thread until its next call into the library.
+ *   - Argument, shape and state checks are synchronous and happen before any
+ *     work is enqueued: a call that returns an error enqueued nothing and left
+ *     the cache's state as it was.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream) and is asynchronous unless stated otherwise.  The caller keeps
+ *     every buffer it passed alive and unmodified until that work finished.
+ *     Faults inside kernels surface at the next synchronising call.
+ *   - Tensor pointers are device pointers owned by the caller, contiguous and
+ *     row-major (innermost dimension last), in the cache's dtype:
+ *       q_blk, out        [B][Hq][Bs][D]
+ *       k_blk, v_blk      [B][Hkv][Bs][D]
+ *       k_prefix,v_prefix [B][Hkv][max_prefix][D]; rows 0..prefix_len-1 are
+ *                         the committed prefix tokens J_out, the rest unused.
+ *     Query head h reads key/value head h / (Hq/Hkv) (grouped-query heads).
+ *   - Softmax: scores are softmax_scale * <q, k>; L values are natural-log
+ *     sum-exp of the scaled scores.  Attention arithmetic is fp32 with bf16
+ *     operands for FB_BF16 (products exact, fp32 accumulation) and fp32
+ *     operands for FB_F32.  A_out and L_out are cached in fp32 for both dtypes.
+ *   - The library keeps no caller pointer after a call returns.  The cache is
+ *     bound to the device that was current at fb_cache_alloc; calls switch to
+ *     it and back.  One cache must not be used by two threads at once.
+ */
+#ifndef FB_H
+#define FB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fb_status;
+enum {
+  FB_OK = 0,
+  FB_E_ARG = 1,          /* null pointer, bad enum, bad number */
+  FB_E_SHAPE = 2,        /* sizes inconsistent or beyond the cache's limits */
+  FB_E_DTYPE = 3,        /* dtype not FB_F32 / FB_BF16 */
+  FB_E_STATE = 4,        /* call not valid in the cache's current state */
+  FB_E_NOMEM = 5,        /* device allocation failed */
+  FB_E_HIP = 6,          /* HIP runtime error or no usable device */
+  FB_E_UNSUPPORTED = 7   /* valid request this build does not implement */
+};
+
+enum { FB_F32 = 0, FB_BF16 = 1 };
+enum { FB_POLICY_ALWAYS = 0, FB_POLICY_TAU = 1, FB_POLICY_GAMMA = 2 };
+enum {
+  FB_FIELD_A_OUT = 0,    /* float [B][Hq][Bs][D]  current cached A_out of every head */
+  FB_FIELD_L_OUT = 1,    /* float [B][Hq][Bs]     current cached L_out */
+  FB_FIELD_SIM = 2,      /* float [B][Hq]         last similarity per head (NaN: none yet) */
+  FB_FIELD_REUSE = 3,    /* uint8 [B][Hq]         1 if the head reused at the last fb_step */
+  FB_FIELD_VALID = 4     /* uint8 [B][Hq]         1 if the head's cache holds a computed A_out */
+};
+
+#define FB_MAX_BATCH 1024     /* sequences per cache */
+#define FB_MAX_HEADS 256      /* query heads per sequence */
+
+typedef struct {
+  int32_t batch;          /* B  >= 1, <= FB_MAX_BATCH */
+  int32_t n_q_heads;      /* Hq >= 1, <= FB_MAX_HEADS, a multiple of n_kv_heads */
+  int32_t n_kv_heads;     /* Hkv >= 1 */
+  int32_t head_dim;       /* D: 64 or 128 (others give FB_E_UNSUPPORTED) */
+  int32_t block_size;     /* Bs >= 1: tokens of the current block */
+  int32_t max_prefix;     /* >= 0: row capacity of the caller's prefix K/V buffers */
+  int32_t dtype;          /* FB_F32 | FB_BF16: dtype of Q/K/V and of the output */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t kv_splits;      /* 0: automatic; else number of prefix chunks per (b, kv head) */
+} fb_config;
+
+typedef struct fb_cache fb_cache;   /* opaque; owns device memory (hipMalloc) */
+
+/* Allocate the A_out/L_out cache for `cfg` on the current device: two fp32
+ * slots of A_out [B][Hq][Bs][D] and L_out [B][Hq][Bs] per head (the second
+ * holds the previous A_out while a similarity is measured), per-head flags,
+ * and scratch for split-prefix partial results sized for max_prefix.  The new
+ * cache is in the reset state.  *out is set only on FB_OK.
+ * Errors: FB_E_ARG (null), FB_E_DTYPE, FB_E_SHAPE, FB_E_UNSUPPORTED,
+ * FB_E_NOMEM, FB_E_HIP (no device). */
+fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out);
+
+/* Release the cache's device memory after waiting for its device to finish
+ * all work.  NULL is a no-op. */
+fb_status fb_cache_free(fb_cache* c);
+
+/* Block boundary (page §1: the next block starts on a prefix that now also
+ * holds the finished block's K/V, appended by the caller).  Marks every head's
+ * cache empty, clears the similarities to NaN and the step counter to 0.
+ * Enqueued on `stream`. */
+fb_status fb_cache_reset(fb_cache* c, void* stream);
+
+/* Block-external attention, page §2 "Mécanisme Central": for every head with
+ * head_mask[b*Hq+h] != 0 (head_mask: device uint8 [B][Hq]; NULL = all heads)
+ * compute A_out (softmax attention of the block queries over prefix rows
+ * 0..prefix_len-1, no mask) and L_out, store them as the head's cached pair,
+ * and mark the head valid.  prefix_len == 0 stores A_out = 0, L_out = -inf.
+ * Errors: FB_E_ARG, FB_E_SHAPE (prefix_len < 0 or > max_prefix). */
+fb_status fb_external_attn(fb_cache* c, const void* q_blk, const void* k_prefix,
+                           const void* v_prefix, int32_t prefix_len,
+                           const uint8_t* head_mask, void* stream);
+
+/* Block-internal bidirectional attention of the block queries over all Bs
+ * block keys (A_in, L_in; no mask), merged in log space with the head's cached
+ * A_out/L_out (page §2, A_full equation), written to `out` in the cache's
+ * dtype.  A head whose cache holds nothing merges with an empty external part,
+ * so its output is A_in.  Errors: FB_E_ARG. */
+fb_status fb_internal_attn_merge(fb_cache* c, const void* q_blk, const void* k_blk,
+                                 const void* v_blk, void* out, void* stream);
+
+typedef struct {
+  int32_t policy;            /* FB_POLICY_* */
+  int32_t tau;               /* TAU: reuse iff the cache holds a computed A_out and
+                                n_updated[b] < tau (strict) */
+  float gamma;               /* GAMMA: reuse iff the head holds a similarity and it
+                                is > gamma (strict) */
+  const int32_t* n_updated;  /* host int32 [B]: tokens of the block updated since the
+                                previous step (TAU only; ignored otherwise) */
+} fb_policy_args;
+
+/* One denoising step (page §2): decide per head whether to reuse the cached
+ * A_out/L_out; recompute block-external attention for the other heads and
+ * refresh their cache; under GAMMA measure each recomputed head's cosine
+ * similarity between its new and previous A_out (flattened over Bs x D) and
+ * decide its reuse at the next step; compute block-internal attention and the
+ * merge into `out`.  The first step after a reset recomputes every head, and
+ * under GAMMA so does the second (a similarity needs two computed A_out).
+ * The whole step is asynchronous on `stream` (GAMMA decisions stay on the
+ * device).  Errors: FB_E_ARG (null, bad policy, tau < 0, n_updated missing or
+ * negative), FB_E_SHAPE, FB_E_STATE (prefix_len differs from the previous
+ * step of the same block). */
+fb_status fb_step(fb_cache* c, const fb_policy_args* p, const void* q_blk, const void* k_blk,
+                  const void* v_blk, const void* k_prefix, const void* v_prefix,
+                  int32_t prefix_len, void* out, void* stream);
+
+/* Copy one field of the cache (layouts in the FB_FIELD_* list) to host
+ * memory `host_dst` of exactly `bytes` bytes, after the work already on
+ * `stream`.  Synchronising; meant for tests and debugging.
+ * Errors: FB_E_ARG (null, unknown field, wrong byte count), FB_E_HIP. */
+fb_status fb_cache_read(const fb_cache* c, int32_t field, void* host_dst, size_t bytes,
+                        void* stream);
+
+/* Device bytes the cache allocated, and the number of prefix chunks
+ * (split-KV) its external attention uses at max_prefix. */
+fb_status fb_cache_info(const fb_cache* c, size_t* device_bytes, int32_t* kv_splits);
+
+/* Kernel timing.  While enabled, every kernel the cache launches is bracketed
+ * by HIP events on its launch stream; fb_profile_read synchronises with them
+ * and returns, per kernel kind, the number of launches and their summed
+ * duration in milliseconds since enabling (and clears the record).  Kinds:
+ * 0 external attention, 1 split combine, 2 internal attention + merge,
+ * 3 similarity / decision, 4 reset.  At most FB_PROFILE_KINDS kinds. */
+#define FB_PROFILE_KINDS 8
+typedef struct {
+  int64_t launches[FB_PROFILE_KINDS];
+  double ms[FB_PROFILE_KINDS];
+} fb_profile_stats;
+fb_status fb_profile_enable(fb_cache* c, int32_t enable);
+fb_status fb_profile_read(fb_cache* c, fb_profile_stats* out);
+
+/* Message of the calling thread's last error ("" after success). */
+const char* fb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FB_H */

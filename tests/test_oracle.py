@@ -1,0 +1,450 @@
+"""Pins of the float64 oracle to things other than itself.
+
+Each ``pin_*`` function checks one fact that the page or plain mathematics
+fixes: a scalar brute force on tiny inputs, an independent library routine
+(torch's float64 scaled_dot_product_attention and logsumexp, scipy's cosine
+distance), closed forms, invariants, and the policy's special cases.  The pins
+look the oracle's functions up on the module at call time, so
+``test_planted_mistakes`` can swap a function for a plausibly wrong one and
+show that some pin fails.  Everything here runs on the CPU.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.spatial.distance
+import torch
+
+import oracle.flashblock as fb
+
+TOL = 1e-12
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- attend
+
+def pin_attend_bruteforce():
+    """Scalar triple loop on tiny inputs: softmax written out term by term."""
+    rng = _rng(1)
+    for (r, n, d) in [(3, 5, 4), (1, 1, 2), (2, 7, 3)]:
+        q, k, v = rng.standard_normal((r, d)), rng.standard_normal((n, d)), rng.standard_normal((n, d))
+        scale = 0.37
+        a, lse = fb.attend(q, k, v, scale)
+        for i in range(r):
+            scores = [scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in range(n)]
+            z = sum(math.exp(sc) for sc in scores)
+            assert abs(lse[i] - math.log(z)) <= TOL
+            for t in range(d):
+                ref = sum(math.exp(scores[j]) * v[j][t] for j in range(n)) / z
+                assert abs(a[i][t] - ref) <= TOL
+
+
+def pin_attend_vs_torch():
+    """torch float64 SDPA (default scale 1/sqrt(D)) and logsumexp."""
+    rng = _rng(2)
+    for (r, n, d) in [(32, 512, 64), (5, 1, 128), (1, 65, 16), (64, 300, 128)]:
+        q, k, v = (rng.standard_normal((r, d)), rng.standard_normal((n, d)),
+                   rng.standard_normal((n, d)))
+        a, lse = fb.attend(q, k, v, fb.default_scale(d))
+        tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, 0].numpy()
+        assert np.max(np.abs(a - ref)) <= TOL
+        ref_l = torch.logsumexp(torch.from_numpy(q @ k.T) / math.sqrt(d), dim=-1).numpy()
+        assert np.max(np.abs(lse - ref_l)) <= 1e-10
+
+
+def pin_external_gqa_vs_torch():
+    """Query head h reads key/value head h // G: torch's enable_gqa mapping."""
+    rng = _rng(3)
+    b, hq, hkv, bs, n, d = 2, 8, 2, 6, 40, 16
+    q = rng.standard_normal((b, hq, bs, d))
+    kp = rng.standard_normal((b, hkv, n + 5, d)) * 2.0
+    vp = rng.standard_normal((b, hkv, n + 5, d))
+    a, lse = fb.external(q, kp, vp, n)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(kp[:, :, :n]).contiguous(),
+        torch.from_numpy(vp[:, :, :n]).contiguous(), enable_gqa=True).numpy()
+    assert np.max(np.abs(a - ref)) <= TOL
+    kr = np.repeat(kp[:, :, :n], hq // hkv, axis=1)
+    ref_l = torch.logsumexp(torch.from_numpy(np.einsum("bhrd,bhnd->bhrn", q, kr)) / math.sqrt(d), -1)
+    assert np.max(np.abs(lse - ref_l.numpy())) <= 1e-10
+
+
+def pin_attend_closed_forms():
+    rng = _rng(4)
+    d = 8
+    # a single key: A = v, L = its score
+    q, k, v = rng.standard_normal((3, d)), rng.standard_normal((1, d)), rng.standard_normal((1, d))
+    a, lse = fb.attend(q, k, v, 0.5)
+    assert np.max(np.abs(a - v[0])) <= TOL
+    assert np.max(np.abs(lse - 0.5 * (q @ k[0]))) <= TOL
+    # constant values: A = that constant whatever the weights
+    k = rng.standard_normal((9, d))
+    v = np.tile(rng.standard_normal(d), (9, 1))
+    a, _ = fb.attend(q, k, v, 0.5)
+    assert np.max(np.abs(a - v[0])) <= TOL
+    # all keys equal: uniform weights, A = mean(V), L = s + ln N
+    k = np.tile(rng.standard_normal(d), (9, 1))
+    v = rng.standard_normal((9, d))
+    a, lse = fb.attend(q, k, v, 0.5)
+    assert np.max(np.abs(a - v.mean(0))) <= TOL
+    assert np.max(np.abs(lse - (0.5 * (q @ k[0]) + math.log(9)))) <= TOL
+    # zero queries: L = ln N exactly, A = mean(V)
+    a, lse = fb.attend(np.zeros((2, d)), rng.standard_normal((9, d)), v, 0.5)
+    assert np.max(np.abs(lse - math.log(9))) <= TOL
+    assert np.max(np.abs(a - v.mean(0))) <= TOL
+    # worked two-key case: scores 0 and ln 3 -> weights 1/4, 3/4, L = ln 4
+    a, lse = fb.attend(np.array([[1.0]]), np.array([[0.0], [math.log(3.0)]]),
+                       np.array([[2.0, -1.0], [6.0, 3.0]]), 1.0)
+    assert np.max(np.abs(a[0] - np.array([5.0, 2.0]))) <= TOL
+    assert abs(lse[0] - math.log(4.0)) <= TOL
+    # huge logits stay finite: the max key dominates, L = its score
+    q = np.array([[30.0] * d])
+    k = np.array([[1.0] * d, [0.5] * d, [-1.0] * d])
+    v = rng.standard_normal((3, d))
+    a, lse = fb.attend(q, k, v, 1.0)
+    assert np.all(np.isfinite(a)) and np.isfinite(lse[0])
+    assert np.max(np.abs(a[0] - v[0])) <= TOL
+    assert abs(lse[0] - 240.0) <= 1e-9
+    # empty key set: no mass
+    a, lse = fb.attend(q, np.zeros((0, d)), np.zeros((0, d)), 1.0)
+    assert np.all(a == 0) and np.all(np.isneginf(lse))
+
+
+def pin_attend_permutation_invariance():
+    rng = _rng(5)
+    q, k, v = rng.standard_normal((4, 16)), rng.standard_normal((33, 16)), rng.standard_normal((33, 16))
+    perm = rng.permutation(33)
+    a1, l1 = fb.attend(q, k, v, 0.25)
+    a2, l2 = fb.attend(q, k[perm], v[perm], 0.25)
+    assert np.max(np.abs(a1 - a2)) <= TOL and np.max(np.abs(l1 - l2)) <= TOL
+
+
+# ---------------------------------------------------------------- merge
+
+def pin_merge_equals_full_attention():
+    """Merging fresh external and internal parts is attention over J_out u J_in."""
+    rng = _rng(6)
+    for (r, n_out, n_in, d, sd) in [(32, 512, 32, 64, 1.0), (16, 1, 16, 128, 3.0),
+                                    (8, 100, 1, 32, 0.1), (5, 2000, 64, 16, 2.0)]:
+        q = rng.standard_normal((r, d)) * sd
+        ko, vo = rng.standard_normal((n_out, d)) * sd, rng.standard_normal((n_out, d))
+        ki, vi = rng.standard_normal((n_in, d)) * sd, rng.standard_normal((n_in, d))
+        scale = fb.default_scale(d)
+        a_o, l_o = fb.attend(q, ko, vo, scale)
+        a_i, l_i = fb.attend(q, ki, vi, scale)
+        a_m, l_m = fb.merge(a_o, l_o, a_i, l_i)
+        a_f, l_f = fb.attend(q, np.concatenate([ko, ki]), np.concatenate([vo, vi]), scale)
+        assert np.max(np.abs(a_m - a_f)) <= TOL
+        assert np.max(np.abs(l_m - l_f)) <= 1e-10
+        assert np.max(np.abs(l_m - np.logaddexp(l_o, l_i))) <= 1e-10
+
+
+def pin_merge_special_cases():
+    rng = _rng(7)
+    q = rng.standard_normal((6, 16))
+    ki, vi = rng.standard_normal((10, 16)), rng.standard_normal((10, 16))
+    a_i, l_i = fb.attend(q, ki, vi, 0.25)
+    a_o, l_o = fb.attend(q, np.zeros((0, 16)), np.zeros((0, 16)), 0.25)
+    a_m, l_m = fb.merge(a_o, l_o, a_i, l_i)      # empty prefix: output = internal part
+    assert np.max(np.abs(a_m - a_i)) <= TOL and np.max(np.abs(l_m - l_i)) <= TOL
+    ko, vo = rng.standard_normal((20, 16)), rng.standard_normal((20, 16))
+    a_o, l_o = fb.attend(q, ko, vo, 0.25)
+    a1, l1 = fb.merge(a_o, l_o, a_i, l_i)
+    a2, l2 = fb.merge(a_i, l_i, a_o, l_o)        # the roles are symmetric
+    assert np.max(np.abs(a1 - a2)) <= TOL and np.max(np.abs(l1 - l2)) <= TOL
+    # equal normalisers: plain average of the two parts
+    a_m, _ = fb.merge(a_o, np.zeros(6), a_i, np.zeros(6))
+    assert np.max(np.abs(a_m - 0.5 * (a_o + a_i))) <= TOL
+    # a part with e^{L} twice the other weighs 2/3
+    a_m, l_m = fb.merge(a_o, np.full(6, math.log(2.0)), a_i, np.zeros(6))
+    assert np.max(np.abs(a_m - (2 * a_o + a_i) / 3)) <= TOL
+    assert np.max(np.abs(l_m - math.log(3.0))) <= TOL
+
+
+def pin_split_associativity():
+    """Splitting J_out into k chunks and merging them in any order gives the unsplit result."""
+    rng = _rng(8)
+    n, d = 97, 32
+    q = rng.standard_normal((7, d))
+    k, v = rng.standard_normal((n, d)) * 1.5, rng.standard_normal((n, d))
+    a_ref, l_ref = fb.attend(q, k, v, 0.2)
+    for chunks in (1, 2, 7, n):
+        bounds = np.linspace(0, n, chunks + 1).astype(int)
+        parts = [fb.attend(q, k[s:e], v[s:e], 0.2) for s, e in zip(bounds[:-1], bounds[1:])]
+        for order in (list(range(chunks)), list(reversed(range(chunks))), list(rng.permutation(chunks))):
+            a, lse = parts[order[0]]
+            for i in order[1:]:
+                a, lse = fb.merge(a, lse, *parts[i])
+            assert np.max(np.abs(a - a_ref)) <= TOL and np.max(np.abs(lse - l_ref)) <= 1e-10
+        # pairwise tree
+        level = list(parts)
+        while len(level) > 1:
+            nxt = [fb.merge(*level[i], *level[i + 1]) for i in range(0, len(level) - 1, 2)]
+            if len(level) % 2:
+                nxt.append(level[-1])
+            level = nxt
+        assert np.max(np.abs(level[0][0] - a_ref)) <= TOL
+
+
+# ---------------------------------------------------------------- cosine
+
+def pin_cosine():
+    rng = _rng(9)
+    for _ in range(5):
+        a, o = rng.standard_normal((4, 8)), rng.standard_normal((4, 8))
+        ref = 1.0 - scipy.spatial.distance.cosine(a.ravel(), o.ravel())
+        assert abs(fb.cosine(a, o) - ref) <= 1e-12
+    a = rng.standard_normal(50)
+    assert abs(fb.cosine(a, 3.0 * a) - 1.0) <= 1e-12
+    assert abs(fb.cosine(a, -a) + 1.0) <= 1e-12
+    assert fb.cosine(a, a) <= 1.0
+    x, y = np.zeros(4), np.zeros(4)
+    x[0], y[1] = 2.0, 5.0
+    assert abs(fb.cosine(x, y)) <= 1e-15
+    assert fb.cosine(np.zeros(3), np.zeros(3)) == 1.0
+    assert fb.cosine(np.zeros(3), np.ones(3)) == 0.0
+    # a vector and a small perturbation of it: 1 - cos ~ |e|^2 sin^2 / 2 > 0
+    e = rng.standard_normal(50) * 1e-3
+    assert 0.0 < 1.0 - fb.cosine(a, a + e) < 1e-5
+
+
+# ---------------------------------------------------------------- policy
+
+def _steps(rng, b, hq, hkv, bs, d, m_list, redraw=True, sd=1.0):
+    """Block inputs where the M rows of each step are redrawn (or kept when redraw=False)."""
+    q = rng.standard_normal((b, hq, bs, d)) * sd
+    k = rng.standard_normal((b, hkv, bs, d)) * sd
+    v = rng.standard_normal((b, hkv, bs, d))
+    steps = []
+    for s, m in enumerate(m_list):
+        m = np.asarray(m)
+        if s > 0 and redraw:
+            for bi in range(b):
+                pos = rng.choice(bs, int(m[bi]), replace=False)
+                q[bi][:, pos] = rng.standard_normal((hq, len(pos), d)) * sd
+                k[bi][:, pos] = rng.standard_normal((hkv, len(pos), d)) * sd
+                v[bi][:, pos] = rng.standard_normal((hkv, len(pos), d))
+        steps.append(fb.StepData(q.copy(), k.copy(), v.copy(), m.astype(np.int32)))
+    return steps
+
+
+def _exact(kp, vp, n, step, b, h, group):
+    g = h // group
+    return fb.attend(step.q[b, h], np.concatenate([kp[b, g, :n], step.k[b, g]]),
+                     np.concatenate([vp[b, g, :n], step.v[b, g]]), fb.default_scale(step.q.shape[-1]))[0]
+
+
+def pin_tau_policy():
+    rng = _rng(10)
+    b, hq, hkv, bs, d, n = 2, 4, 2, 8, 16, 40
+    kp, vp = rng.standard_normal((b, hkv, n, d)), rng.standard_normal((b, hkv, n, d))
+    m_list = [[0, 0], [3, 0], [4, 1], [5, 4], [0, 8], [4, 3], [2, 4]]
+    steps = _steps(rng, b, hq, hkv, bs, d, m_list)
+    tau = 4
+    res = fb.run_block(kp, vp, n, steps, fb.TAU, tau=tau)
+    for s, m in enumerate(m_list):
+        for bi in range(b):
+            expect = 0 if s == 0 else int(m[bi] < tau)     # strict: M == tau recomputes
+            assert np.all(res.reuse[s, bi] == expect), (s, bi)
+    # number of reuse steps = sum over s >= 1 of [M_s < tau]
+    for bi in range(b):
+        assert int(res.reuse[:, bi, 0].sum()) == sum(int(m[bi] < tau) for m in m_list[1:])
+    # tau = 0: never reuse, every output is exact attention over J_out u J_in
+    res0 = fb.run_block(kp, vp, n, steps, fb.TAU, tau=0)
+    assert np.all(res0.reuse == 0)
+    for s, st in enumerate(steps):
+        for bi, h in itertools.product(range(b), range(hq)):
+            assert np.max(np.abs(res0.out[s, bi, h] - _exact(kp, vp, n, st, bi, h, hq // hkv))) <= TOL
+    # always: never reuse either
+    assert np.all(fb.run_block(kp, vp, n, steps, fb.ALWAYS).reuse == 0)
+    # tau > Bs: every step after the first reuses, and the cache keeps step 0's A_out
+    resb = fb.run_block(kp, vp, n, steps, fb.TAU, tau=bs + 1)
+    assert np.all(resb.reuse[0] == 0) and np.all(resb.reuse[1:] == 1)
+    for s in range(1, len(steps)):
+        assert np.array_equal(resb.a_out[s], resb.a_out[0])
+        assert np.array_equal(resb.l_out[s], resb.l_out[0])
+    # a reuse step with changed queries is not exact attention (the cache is stale)
+    assert np.max(np.abs(resb.out[1, 0] - res0.out[1, 0])) > 1e-6
+    # M = 0 at every step: nothing changes, every step after 0 reuses and stays exact
+    steps0 = _steps(rng, b, hq, hkv, bs, d, [[0, 0]] * 5)
+    resz = fb.run_block(kp, vp, n, steps0, fb.TAU, tau=1)
+    assert np.all(resz.reuse[1:] == 1)
+    for s, st in enumerate(steps0):
+        for bi, h in itertools.product(range(b), range(hq)):
+            assert np.max(np.abs(resz.out[s, bi, h] - _exact(kp, vp, n, st, bi, h, hq // hkv))) <= TOL
+
+
+def _video_steps(rng, hq, bs, d, sigma, n_steps):
+    qb = rng.standard_normal((1, hq, bs, d))
+    k = rng.standard_normal((1, hq, bs, d))
+    v = rng.standard_normal((1, hq, bs, d))
+    steps = []
+    for _ in range(n_steps):
+        q = qb + sigma[None, :, None, None] * rng.standard_normal(qb.shape)
+        steps.append(fb.StepData(q, k, v, np.full(1, bs, dtype=np.int32)))
+    return steps
+
+
+def pin_gamma_policy():
+    rng = _rng(11)
+    hq, bs, d, n = 3, 6, 8, 30
+    kp, vp = rng.standard_normal((1, hq, n, d)), rng.standard_normal((1, hq, n, d))
+    # sigma = 0: the queries never change, sim = 1 > gamma, the head reuses from step 2 on
+    steps = _video_steps(rng, hq, bs, d, np.zeros(hq), 5)
+    res = fb.run_block(kp, vp, n, steps, fb.GAMMA, gamma=0.95)
+    assert np.all(res.reuse[:2] == 0) and np.all(res.reuse[2:] == 1)
+    assert np.all(np.abs(res.sim[1:] - 1.0) <= 1e-12) and np.all(np.isnan(res.sim[0]))
+    # gamma = 1 never reuses (strict, cosine <= 1)
+    assert np.all(fb.run_block(kp, vp, n, steps, fb.GAMMA, gamma=1.0).reuse == 0)
+    # gamma = -1: every head reuses from step 2 whatever its queries do
+    steps = _video_steps(rng, hq, bs, d, np.array([0.05, 1.0, 5.0]), 5)
+    res = fb.run_block(kp, vp, n, steps, fb.GAMMA, gamma=-1.0)
+    assert np.all(res.reuse[:2] == 0) and np.all(res.reuse[2:] == 1)
+    # mixed: a quiet head reuses, a loud one keeps recomputing, sims match scipy
+    res = fb.run_block(kp, vp, n, steps, fb.GAMMA, gamma=0.95)
+    assert res.reuse[2, 0, 0] == 1 and np.all(res.reuse[:, 0, 2] == 0)
+    for s in range(1, 5):
+        if res.reuse[s, 0, 2] == 0:
+            ref = fb.attend(steps[s - 1].q[0, 2], kp[0, 2], vp[0, 2], fb.default_scale(d))[0]
+            new = fb.attend(steps[s].q[0, 2], kp[0, 2], vp[0, 2], fb.default_scale(d))[0]
+            assert abs(res.sim[s, 0, 2] - (1 - scipy.spatial.distance.cosine(new.ravel(), ref.ravel()))) < 1e-12
+
+
+def pin_multi_block_append():
+    """Block end: the block's final K/V join the prefix and the caches restart."""
+    rng = _rng(12)
+    b, hq, hkv, bs, d, n = 1, 2, 1, 4, 8, 10
+    kp, vp = rng.standard_normal((b, hkv, n, d)), rng.standard_normal((b, hkv, n, d))
+    blk1 = _steps(rng, b, hq, hkv, bs, d, [[0], [1], [4]])
+    blk2 = _steps(rng, b, hq, hkv, bs, d, [[0], [0], [2]])
+    r1, r2 = fb.run_blocks(kp, vp, [blk1, blk2], fb.TAU, tau=3)
+    assert np.all(r2.reuse[0] == 0)                    # fresh block: no reuse at its first step
+    kp2 = np.concatenate([kp, blk1[-1].k], axis=2)
+    vp2 = np.concatenate([vp, blk1[-1].v], axis=2)
+    for h in range(hq):
+        assert np.max(np.abs(r2.out[0, 0, h] - _exact(kp2, vp2, n + bs, blk2[0], 0, h, hq))) <= TOL
+
+
+PINS = [pin_attend_bruteforce, pin_attend_vs_torch, pin_external_gqa_vs_torch, pin_attend_closed_forms,
+        pin_attend_permutation_invariance, pin_merge_equals_full_attention, pin_merge_special_cases,
+        pin_split_associativity, pin_cosine, pin_tau_policy, pin_gamma_policy, pin_multi_block_append]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+_real_attend, _real_merge, _real_cosine, _real_decide = fb.attend, fb.merge, fb.cosine, fb.decide
+
+
+def _attend_no_max_shift(q, k, v, scale):
+    s = scale * (q @ k.T)
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = np.exp(s)
+        z = p.sum(1)
+        return (p @ v) / z[:, None], np.log(z)
+
+
+def _attend_log2(q, k, v, scale):
+    a, lse = _real_attend(q, k, v, scale)
+    return a, lse / math.log(2.0)
+
+
+def _attend_no_scale(q, k, v, scale):
+    return _real_attend(q, k, v, 1.0)
+
+
+def _attend_kv_swapped(q, k, v, scale):
+    return _real_attend(q, v, k, scale)
+
+
+def _attend_unnormalised(q, k, v, scale):
+    a, lse = _real_attend(q, k, v, scale)
+    return a * np.exp(lse)[:, None] if k.shape[0] else a, lse
+
+
+def _merge_sign(a_out, l_out, a_in, l_in):
+    m = np.maximum(l_out, l_in)
+    w_o, w_i = np.exp(m - l_out), np.exp(m - l_in)
+    return (w_o[:, None] * a_out + w_i[:, None] * a_in) / (w_o + w_i)[:, None], m + np.log(w_o + w_i)
+
+
+def _merge_no_denominator(a_out, l_out, a_in, l_in):
+    m = np.maximum(l_out, l_in)
+    w_o, w_i = np.exp(l_out - m), np.exp(l_in - m)
+    return w_o[:, None] * a_out + w_i[:, None] * a_in, m + np.log(w_o + w_i)
+
+
+def _merge_drop_in(a_out, l_out, a_in, l_in):
+    return _real_merge(a_out, l_out, np.zeros_like(a_in), l_in)
+
+
+def _decide_le(policy, st, n_updated, tau, gamma):
+    if policy == fb.TAU and st.valid:
+        return n_updated <= tau
+    return _real_decide(policy, st, n_updated, tau, gamma)
+
+
+def _decide_ge(policy, st, n_updated, tau, gamma):
+    if policy == fb.GAMMA and st.valid:
+        return st.sim is not None and st.sim >= gamma
+    return _real_decide(policy, st, n_updated, tau, gamma)
+
+
+def _decide_ignore_valid(policy, st, n_updated, tau, gamma):
+    if policy == fb.TAU:
+        return n_updated < tau
+    return _real_decide(policy, st, n_updated, tau, gamma)
+
+
+def _cosine_unclamped_l1(a, o):
+    a, o = np.ravel(a), np.ravel(o)
+    na, no = np.abs(a).sum(), np.abs(o).sum()
+    return float(np.dot(a, o) / (na * no)) if na and no else 1.0
+
+
+def _cosine_no_abs(a, o):
+    return abs(_real_cosine(a, o))
+
+
+def _external_mod_group(q, k_prefix, v_prefix, n_prefix, scale=None):
+    bsz, hq, bs, d = q.shape
+    hkv = k_prefix.shape[1]
+    a, lse = np.empty((bsz, hq, bs, d)), np.empty((bsz, hq, bs))
+    for b in range(bsz):
+        for h in range(hq):
+            a[b, h], lse[b, h] = _real_attend(q[b, h], k_prefix[b, h % hkv, :n_prefix],
+                                              v_prefix[b, h % hkv, :n_prefix], fb.default_scale(d))
+    return a, lse
+
+
+MUTANTS = [
+    ("attend", _attend_no_max_shift), ("attend", _attend_log2), ("attend", _attend_no_scale),
+    ("attend", _attend_kv_swapped), ("attend", _attend_unnormalised),
+    ("merge", _merge_sign), ("merge", _merge_no_denominator), ("merge", _merge_drop_in),
+    ("decide", _decide_le), ("decide", _decide_ge), ("decide", _decide_ignore_valid),
+    ("cosine", _cosine_unclamped_l1), ("cosine", _cosine_no_abs),
+    ("external", _external_mod_group),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=[m.__name__ for _, m in MUTANTS])
+def test_planted_mistakes(monkeypatch, name, mutant):
+    """Every plausible mistake planted in the oracle makes at least one pin fail."""
+    monkeypatch.setattr(fb, name, mutant)
+    failed = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, FloatingPointError, ValueError, IndexError, TypeError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {mutant.__name__}"
