@@ -1,0 +1,100 @@
+// Parameter blocks and launchers shared by the host runtime (fb_runtime.cpp)
+// and the gfx950 kernels (fb_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fb.h"
+
+namespace fbk {
+
+constexpr int kThreads = 256;     // 4 wave64 per workgroup
+constexpr int kRowTile = 128;     // packed query rows per attention workgroup (32 per wave)
+constexpr int kKeyTile = 64;      // keys staged in LDS per iteration
+constexpr int kCombineRows = 32;  // rows of one head per combine workgroup
+constexpr int kMaxSplits = 64;
+
+// Which heads a launch works on.  A head (b, h) is selected when bit b of
+// `seq_bits` is set and, if `flags` is not null, (flags[b*Hq+h] != 0) equals
+// `flags_select`.
+struct HeadSel {
+  uint32_t seq_bits[FB_MAX_BATCH / 32];
+  const uint8_t* flags;
+  int32_t flags_select;
+};
+
+// Attention of packed query rows over one key range.  The G = Hq/Hkv query
+// heads of kv head g are contiguous in [B][Hq][Bs][D], so the G*Bs rows of a
+// (b, g) group form one contiguous [G*Bs][D] matrix ("packed rows").
+struct AttnParams {
+  const void* q;          // [B][Hq][Bs][D]
+  const void* k;          // [B][Hkv][kv_cap][D]
+  const void* v;
+  int64_t kv_cap;         // rows per (b, kv head) in k/v
+  int32_t n_keys;         // keys 0..n_keys-1 are attended
+  int32_t batch, hq, hkv, bs, rows;   // rows = (Hq/Hkv) * Bs
+  int32_t row_tiles;      // ceil(rows / kRowTile)
+  int32_t splits;         // key ranges per group
+  int32_t keys_per_split; // multiple of kKeyTile
+  float scale_log2;       // softmax scale * log2(e)
+  HeadSel sel;
+  // partial epilogue: normalised A and natural-log L per split
+  float* part_o;          // [splits][B][Hq][Bs][D]
+  float* part_l;          // [splits][B][Hq][Bs]
+  int64_t part_o_stride, part_l_stride;
+  // merge epilogue
+  const float* slot_o;    // [2][B][Hq][Bs][D]
+  const float* slot_l;    // [2][B][Hq][Bs]
+  int64_t slot_o_stride, slot_l_stride;
+  const uint8_t* cur;     // [B][Hq] current slot
+  const uint8_t* valid;   // [B][Hq]
+  void* out;              // [B][Hq][Bs][D]
+  uint8_t* reuse_rec;     // [B][Hq] or null: 1 - selected(b, h) is recorded
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_l;
+  int64_t part_o_stride, part_l_stride;
+  int32_t splits, batch, hq, bs, row_chunks;
+  HeadSel sel;
+  float* slot_o;
+  float* slot_l;
+  int64_t slot_o_stride, slot_l_stride;
+  uint8_t* cur;
+  uint8_t* valid;
+  int32_t to_other_slot;  // 1: write slot cur^1 and sum similarity terms (gamma)
+  float* cos_part;        // [B*Hq][row_chunks][3]
+};
+
+struct DecideParams {
+  int32_t n_heads;        // B*Hq
+  int32_t hq, row_chunks;
+  const uint8_t* reuse_now;  // decisions applied at this step
+  uint8_t* reuse_next;       // decisions for the next step
+  uint8_t* cur;
+  uint8_t* valid;
+  float* sim;
+  const float* cos_part;
+  float gamma;
+};
+
+struct ResetParams {
+  int32_t n_heads;
+  uint8_t* cur;
+  uint8_t* valid;
+  uint8_t* reuse;         // [2][B*Hq]
+  float* sim;
+};
+
+enum AttnMode { kModePartial = 0, kModeMerge = 1 };
+
+// Launchers (fb_kernels.hip).  Return the launch status.
+hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, hipStream_t s);
+hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s);
+hipError_t launch_decide(const DecideParams& p, hipStream_t s);
+hipError_t launch_reset(const ResetParams& p, hipStream_t s);
+
+}  // namespace fbk

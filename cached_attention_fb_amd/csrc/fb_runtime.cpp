@@ -1,0 +1,561 @@
+// Host runtime of libfb.so: argument checks, the A_out/L_out cache, the reuse
+// policy state, split-KV planning and stream-ordered launches.  The C ABI and
+// its contract are in include/fb.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "fb.h"
+#include "fb_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+fb_status fail(fb_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+fb_status ok() {
+  g_err.clear();
+  return FB_OK;
+}
+
+fb_status hip_fail(hipError_t e, const char* what) {
+  return fail(FB_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Switches to the cache's device for the duration of a call.
+struct DeviceGuard {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int now = -1;
+    if (prev >= 0 && hipGetDevice(&now) == hipSuccess && now != prev) (void)hipSetDevice(prev);
+  }
+};
+
+struct ProfRec {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct fb_cache {
+  fb_config cfg{};
+  int device = 0;
+  int group = 1;         // Hq / Hkv
+  int rows = 0;          // packed rows per (b, kv head) = group * Bs
+  int row_tiles = 0;
+  int row_chunks = 0;    // combine workgroups per head
+  int splits_cap = 1;    // splits the scratch is sized for
+  float scale = 0.0f;
+  size_t bytes = 0;
+  // device memory
+  float* slot_o = nullptr;   // [2][B][Hq][Bs][D]
+  float* slot_l = nullptr;   // [2][B][Hq][Bs]
+  uint8_t* cur = nullptr;    // [B][Hq]
+  uint8_t* valid = nullptr;  // [B][Hq]
+  uint8_t* reuse = nullptr;  // [2][B][Hq], indexed by step parity
+  float* sim = nullptr;      // [B][Hq]
+  float* part_o = nullptr;   // [splits_cap][B][Hq][Bs][D]
+  float* part_l = nullptr;   // [splits_cap][B][Hq][Bs]
+  float* cos_part = nullptr; // [B][Hq][row_chunks][3]
+  // host state
+  int64_t steps = 0;         // fb_step calls since the last reset
+  int32_t block_prefix = -1; // prefix_len of the current block
+  int32_t block_policy = -1;
+  std::vector<uint8_t> host_valid;   // [B]: every head of b holds a computed A_out (tau bookkeeping)
+  // profiling
+  bool prof = false;
+  std::vector<ProfRec> prof_recs;
+  int64_t prof_launches[FB_PROFILE_KINDS] = {};
+  double prof_ms[FB_PROFILE_KINDS] = {};
+};
+
+namespace {
+
+int64_t elems_per_slot(const fb_config& c) {
+  return (int64_t)c.batch * c.n_q_heads * c.block_size * c.head_dim;
+}
+int64_t rows_per_slot(const fb_config& c) { return (int64_t)c.batch * c.n_q_heads * c.block_size; }
+
+fb_status check_config(const fb_config* cfg) {
+  if (!cfg) return fail(FB_E_ARG, "config is null");
+  if (cfg->dtype != FB_F32 && cfg->dtype != FB_BF16) return fail(FB_E_DTYPE, "dtype %d is not FB_F32 or FB_BF16", cfg->dtype);
+  if (cfg->batch < 1 || cfg->batch > FB_MAX_BATCH) return fail(FB_E_SHAPE, "batch %d outside [1, %d]", cfg->batch, FB_MAX_BATCH);
+  if (cfg->n_kv_heads < 1 || cfg->n_q_heads < 1 || cfg->n_q_heads > FB_MAX_HEADS)
+    return fail(FB_E_SHAPE, "heads q=%d kv=%d invalid", cfg->n_q_heads, cfg->n_kv_heads);
+  if (cfg->n_q_heads % cfg->n_kv_heads != 0)
+    return fail(FB_E_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", cfg->n_q_heads, cfg->n_kv_heads);
+  if (cfg->block_size < 1 || cfg->block_size > (1 << 20)) return fail(FB_E_SHAPE, "block_size %d invalid", cfg->block_size);
+  if (cfg->max_prefix < 0) return fail(FB_E_SHAPE, "max_prefix %d is negative", cfg->max_prefix);
+  if (cfg->kv_splits < 0 || cfg->kv_splits > fbk::kMaxSplits)
+    return fail(FB_E_ARG, "kv_splits %d outside [0, %d]", cfg->kv_splits, fbk::kMaxSplits);
+  if (!(cfg->softmax_scale == cfg->softmax_scale) || std::isinf(cfg->softmax_scale))
+    return fail(FB_E_ARG, "softmax_scale is not finite");
+  if (cfg->head_dim != 64 && cfg->head_dim != 128)
+    return fail(FB_E_UNSUPPORTED, "head_dim %d: this build supports 64 and 128", cfg->head_dim);
+  const int64_t rows = (int64_t)(cfg->n_q_heads / cfg->n_kv_heads) * cfg->block_size;
+  if (rows > (1 << 24)) return fail(FB_E_SHAPE, "packed rows %lld too many", (long long)rows);
+  return FB_OK;
+}
+
+// Number of prefix chunks: enough workgroups to fill 256 CUs, at least two
+// 64-key tiles per chunk, at most the scratch capacity.
+int choose_splits(const fb_cache* c, int n_keys, int active_groups) {
+  const int tiles = (n_keys + fbk::kKeyTile - 1) / fbk::kKeyTile;
+  if (tiles <= 1) return 1;
+  int want;
+  if (c->cfg.kv_splits > 0) {
+    want = c->cfg.kv_splits;
+  } else {
+    const int base = std::max(1, active_groups * c->row_tiles);
+    want = (256 + base - 1) / base;
+    want = std::min(want, std::max(1, tiles / 2));
+  }
+  want = std::max(1, std::min({want, tiles, c->splits_cap}));
+  const int tiles_per = (tiles + want - 1) / want;
+  return (tiles + tiles_per - 1) / tiles_per;   // no empty chunk
+}
+
+void prof_begin(fb_cache* c, hipStream_t s, ProfRec* r, int kind) {
+  r->kind = -1;
+  if (!c->prof) return;
+  if (hipEventCreate(&r->start) != hipSuccess) return;
+  if (hipEventCreate(&r->stop) != hipSuccess) {
+    (void)hipEventDestroy(r->start);
+    return;
+  }
+  r->kind = kind;
+  (void)hipEventRecord(r->start, s);
+}
+void prof_end(fb_cache* c, hipStream_t s, ProfRec* r) {
+  if (r->kind < 0) return;
+  (void)hipEventRecord(r->stop, s);
+  c->prof_recs.push_back(*r);
+}
+
+fbk::HeadSel all_heads(const fb_cache* c) {
+  fbk::HeadSel h{};
+  for (int b = 0; b < c->cfg.batch; ++b) h.seq_bits[b >> 5] |= 1u << (b & 31);
+  h.flags = nullptr;
+  h.flags_select = 1;
+  return h;
+}
+
+fbk::AttnParams attn_common(const fb_cache* c, const void* q) {
+  fbk::AttnParams p{};
+  p.q = q;
+  p.batch = c->cfg.batch;
+  p.hq = c->cfg.n_q_heads;
+  p.hkv = c->cfg.n_kv_heads;
+  p.bs = c->cfg.block_size;
+  p.rows = c->rows;
+  p.row_tiles = c->row_tiles;
+  p.scale_log2 = c->scale * 1.4426950408889634f;
+  return p;
+}
+
+fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* vp, int32_t n,
+                       const fbk::HeadSel& sel, int active_groups, bool gamma, hipStream_t s) {
+  fbk::AttnParams p = attn_common(c, q);
+  p.k = kp;
+  p.v = vp;
+  p.kv_cap = c->cfg.max_prefix;
+  p.n_keys = n;
+  p.splits = choose_splits(c, n, active_groups);
+  const int tiles = (n + fbk::kKeyTile - 1) / fbk::kKeyTile;
+  p.keys_per_split = std::max(1, (tiles + p.splits - 1) / p.splits) * fbk::kKeyTile;
+  p.sel = sel;
+  p.part_o = c->part_o;
+  p.part_l = c->part_l;
+  p.part_o_stride = elems_per_slot(c->cfg);
+  p.part_l_stride = rows_per_slot(c->cfg);
+  ProfRec r;
+  prof_begin(c, s, &r, 0);
+  hipError_t e = fbk::launch_attn(c->cfg.dtype, c->cfg.head_dim, fbk::kModePartial, p, s);
+  prof_end(c, s, &r);
+  if (e != hipSuccess) return hip_fail(e, "external attention launch");
+
+  fbk::CombineParams cp{};
+  cp.part_o = c->part_o;
+  cp.part_l = c->part_l;
+  cp.part_o_stride = p.part_o_stride;
+  cp.part_l_stride = p.part_l_stride;
+  cp.splits = p.splits;
+  cp.batch = c->cfg.batch;
+  cp.hq = c->cfg.n_q_heads;
+  cp.bs = c->cfg.block_size;
+  cp.row_chunks = c->row_chunks;
+  cp.sel = sel;
+  cp.slot_o = c->slot_o;
+  cp.slot_l = c->slot_l;
+  cp.slot_o_stride = elems_per_slot(c->cfg);
+  cp.slot_l_stride = rows_per_slot(c->cfg);
+  cp.cur = c->cur;
+  cp.valid = c->valid;
+  cp.to_other_slot = gamma ? 1 : 0;
+  cp.cos_part = c->cos_part;
+  prof_begin(c, s, &r, 1);
+  e = fbk::launch_combine(c->cfg.head_dim, cp, s);
+  prof_end(c, s, &r);
+  if (e != hipSuccess) return hip_fail(e, "split combine launch");
+  return FB_OK;
+}
+
+fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* vb, void* out,
+                       const fbk::HeadSel& rec_sel, uint8_t* reuse_rec, hipStream_t s) {
+  fbk::AttnParams p = attn_common(c, q);
+  p.k = kb;
+  p.v = vb;
+  p.kv_cap = c->cfg.block_size;
+  p.n_keys = c->cfg.block_size;
+  p.splits = 1;
+  p.keys_per_split = ((c->cfg.block_size + fbk::kKeyTile - 1) / fbk::kKeyTile) * fbk::kKeyTile;
+  p.sel = rec_sel;
+  p.slot_o = c->slot_o;
+  p.slot_l = c->slot_l;
+  p.slot_o_stride = elems_per_slot(c->cfg);
+  p.slot_l_stride = rows_per_slot(c->cfg);
+  p.cur = c->cur;
+  p.valid = c->valid;
+  p.out = out;
+  p.reuse_rec = reuse_rec;
+  ProfRec r;
+  prof_begin(c, s, &r, 2);
+  hipError_t e = fbk::launch_attn(c->cfg.dtype, c->cfg.head_dim, fbk::kModeMerge, p, s);
+  prof_end(c, s, &r);
+  if (e != hipSuccess) return hip_fail(e, "internal attention launch");
+  return FB_OK;
+}
+
+fb_status run_reset(fb_cache* c, hipStream_t s) {
+  fbk::ResetParams rp{};
+  rp.n_heads = c->cfg.batch * c->cfg.n_q_heads;
+  rp.cur = c->cur;
+  rp.valid = c->valid;
+  rp.reuse = c->reuse;
+  rp.sim = c->sim;
+  ProfRec r;
+  prof_begin(c, s, &r, 4);
+  hipError_t e = fbk::launch_reset(rp, s);
+  prof_end(c, s, &r);
+  if (e != hipSuccess) return hip_fail(e, "reset launch");
+  c->steps = 0;
+  c->block_prefix = -1;
+  c->block_policy = -1;
+  std::fill(c->host_valid.begin(), c->host_valid.end(), 0);
+  return FB_OK;
+}
+
+void free_all(fb_cache* c) {
+  void* ptrs[] = {c->slot_o, c->slot_l, c->cur, c->valid, c->reuse, c->sim, c->part_o, c->part_l, c->cos_part};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  for (auto& r : c->prof_recs) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fb_last_error(void) { return g_err.c_str(); }
+
+fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
+  if (!out) return fail(FB_E_ARG, "out is null");
+  fb_status st = check_config(cfg);
+  if (st != FB_OK) return st;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "no usable HIP device");
+  int ndev = 0;
+  e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev < 1) return fail(FB_E_HIP, "no usable HIP device");
+
+  fb_cache* c = new (std::nothrow) fb_cache();
+  if (!c) return fail(FB_E_NOMEM, "host allocation failed");
+  c->cfg = *cfg;
+  c->device = dev;
+  c->group = cfg->n_q_heads / cfg->n_kv_heads;
+  c->rows = c->group * cfg->block_size;
+  c->row_tiles = (c->rows + fbk::kRowTile - 1) / fbk::kRowTile;
+  c->row_chunks = (cfg->block_size + fbk::kCombineRows - 1) / fbk::kCombineRows;
+  c->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
+  c->host_valid.assign(cfg->batch, 0);
+  c->splits_cap = fbk::kMaxSplits;
+  c->splits_cap = choose_splits(c, cfg->max_prefix, cfg->batch * cfg->n_kv_heads);
+  if (cfg->kv_splits > 0) c->splits_cap = std::max(c->splits_cap, std::min(cfg->kv_splits, fbk::kMaxSplits));
+
+  const int64_t nh = (int64_t)cfg->batch * cfg->n_q_heads;
+  const size_t so = elems_per_slot(*cfg) * sizeof(float), sl = rows_per_slot(*cfg) * sizeof(float);
+  struct {
+    void** p;
+    size_t n;
+  } plan[] = {
+      {(void**)&c->slot_o, 2 * so},
+      {(void**)&c->slot_l, 2 * sl},
+      {(void**)&c->cur, (size_t)nh},
+      {(void**)&c->valid, (size_t)nh},
+      {(void**)&c->reuse, (size_t)(2 * nh)},
+      {(void**)&c->sim, (size_t)nh * sizeof(float)},
+      {(void**)&c->part_o, (size_t)c->splits_cap * so},
+      {(void**)&c->part_l, (size_t)c->splits_cap * sl},
+      {(void**)&c->cos_part, (size_t)nh * c->row_chunks * 3 * sizeof(float)},
+  };
+  for (auto& a : plan) {
+    e = hipMalloc(a.p, std::max<size_t>(a.n, 256));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      free_all(c);
+      delete c;
+      return fail(FB_E_NOMEM, "device allocation of %zu bytes failed: %s", a.n, hipGetErrorString(e));
+    }
+    c->bytes += a.n;
+  }
+  st = run_reset(c, nullptr);
+  if (st == FB_OK) {
+    e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess) st = hip_fail(e, "cache initialisation");
+  }
+  if (st != FB_OK) {
+    free_all(c);
+    delete c;
+    return st;
+  }
+  *out = c;
+  return ok();
+}
+
+fb_status fb_cache_free(fb_cache* c) {
+  if (!c) return ok();
+  DeviceGuard g(c->device);
+  (void)hipDeviceSynchronize();
+  free_all(c);
+  delete c;
+  return ok();
+}
+
+fb_status fb_cache_reset(fb_cache* c, void* stream) {
+  if (!c) return fail(FB_E_ARG, "cache is null");
+  DeviceGuard g(c->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "set device");
+  fb_status st = run_reset(c, (hipStream_t)stream);
+  return st == FB_OK ? ok() : st;
+}
+
+fb_status fb_external_attn(fb_cache* c, const void* q_blk, const void* k_prefix, const void* v_prefix,
+                           int32_t prefix_len, const uint8_t* head_mask, void* stream) {
+  if (!c) return fail(FB_E_ARG, "cache is null");
+  if (!q_blk) return fail(FB_E_ARG, "q_blk is null");
+  if (prefix_len < 0 || prefix_len > c->cfg.max_prefix)
+    return fail(FB_E_SHAPE, "prefix_len %d outside [0, max_prefix=%d]", prefix_len, c->cfg.max_prefix);
+  if (prefix_len > 0 && (!k_prefix || !v_prefix)) return fail(FB_E_ARG, "k_prefix/v_prefix is null");
+  DeviceGuard g(c->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "set device");
+  fbk::HeadSel sel = all_heads(c);
+  sel.flags = head_mask;
+  sel.flags_select = 1;
+  fb_status st = run_external(c, q_blk, k_prefix, v_prefix, prefix_len, sel,
+                              c->cfg.batch * c->cfg.n_kv_heads, false, (hipStream_t)stream);
+  if (st != FB_OK) return st;
+  std::fill(c->host_valid.begin(), c->host_valid.end(), head_mask ? 0 : 1);
+  return ok();
+}
+
+fb_status fb_internal_attn_merge(fb_cache* c, const void* q_blk, const void* k_blk, const void* v_blk,
+                                 void* out, void* stream) {
+  if (!c) return fail(FB_E_ARG, "cache is null");
+  if (!q_blk || !k_blk || !v_blk || !out) return fail(FB_E_ARG, "a tensor pointer is null");
+  DeviceGuard g(c->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "set device");
+  fb_status st = run_internal(c, q_blk, k_blk, v_blk, out, all_heads(c), nullptr, (hipStream_t)stream);
+  return st == FB_OK ? ok() : st;
+}
+
+fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, const void* k_blk,
+                  const void* v_blk, const void* k_prefix, const void* v_prefix, int32_t prefix_len,
+                  void* out, void* stream) {
+  if (!c) return fail(FB_E_ARG, "cache is null");
+  if (!pa) return fail(FB_E_ARG, "policy args are null");
+  if (!q_blk || !k_blk || !v_blk || !out) return fail(FB_E_ARG, "a tensor pointer is null");
+  if (pa->policy != FB_POLICY_ALWAYS && pa->policy != FB_POLICY_TAU && pa->policy != FB_POLICY_GAMMA)
+    return fail(FB_E_ARG, "unknown policy %d", pa->policy);
+  if (prefix_len < 0 || prefix_len > c->cfg.max_prefix)
+    return fail(FB_E_SHAPE, "prefix_len %d outside [0, max_prefix=%d]", prefix_len, c->cfg.max_prefix);
+  if (prefix_len > 0 && (!k_prefix || !v_prefix)) return fail(FB_E_ARG, "k_prefix/v_prefix is null");
+  if (c->steps > 0 && prefix_len != c->block_prefix)
+    return fail(FB_E_STATE, "prefix_len %d differs from %d used earlier in this block (reset first)",
+                prefix_len, c->block_prefix);
+  if (c->steps > 0 && pa->policy != c->block_policy)
+    return fail(FB_E_STATE, "policy changed inside a block (reset first)");
+  const int B = c->cfg.batch;
+  std::vector<uint8_t> recompute(B, 1);
+  if (pa->policy == FB_POLICY_TAU) {
+    if (pa->tau < 0) return fail(FB_E_ARG, "tau %d is negative", pa->tau);
+    if (!pa->n_updated) return fail(FB_E_ARG, "n_updated is null under the tau policy");
+    for (int b = 0; b < B; ++b) {
+      if (pa->n_updated[b] < 0) return fail(FB_E_ARG, "n_updated[%d] = %d is negative", b, pa->n_updated[b]);
+      recompute[b] = (c->host_valid[b] && pa->n_updated[b] < pa->tau) ? 0 : 1;
+    }
+  }
+  if (pa->policy == FB_POLICY_GAMMA && !(pa->gamma == pa->gamma)) return fail(FB_E_ARG, "gamma is NaN");
+  DeviceGuard g(c->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "set device");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nh = (int64_t)B * c->cfg.n_q_heads;
+  uint8_t* reuse_now = c->reuse + (c->steps & 1) * nh;
+  uint8_t* reuse_next = c->reuse + ((c->steps + 1) & 1) * nh;
+
+  fb_status st = FB_OK;
+  fbk::HeadSel sel{};
+  if (pa->policy == FB_POLICY_GAMMA) {
+    sel = all_heads(c);
+    sel.flags = reuse_now;
+    sel.flags_select = 0;   // compute the heads not marked for reuse
+    st = run_external(c, q_blk, k_prefix, v_prefix, prefix_len, sel, B * c->cfg.n_kv_heads, true, s);
+    if (st != FB_OK) return st;
+    fbk::DecideParams dp{};
+    dp.n_heads = (int32_t)nh;
+    dp.hq = c->cfg.n_q_heads;
+    dp.row_chunks = c->row_chunks;
+    dp.reuse_now = reuse_now;
+    dp.reuse_next = reuse_next;
+    dp.cur = c->cur;
+    dp.valid = c->valid;
+    dp.sim = c->sim;
+    dp.cos_part = c->cos_part;
+    dp.gamma = pa->gamma;
+    ProfRec r;
+    prof_begin(c, s, &r, 3);
+    hipError_t e = fbk::launch_decide(dp, s);
+    prof_end(c, s, &r);
+    if (e != hipSuccess) return hip_fail(e, "decision launch");
+    st = run_internal(c, q_blk, k_blk, v_blk, out, sel, nullptr, s);
+  } else {
+    int active = 0;
+    for (int b = 0; b < B; ++b) {
+      if (recompute[b]) {
+        sel.seq_bits[b >> 5] |= 1u << (b & 31);
+        ++active;
+      }
+    }
+    sel.flags = nullptr;
+    sel.flags_select = 1;
+    if (active > 0) {
+      st = run_external(c, q_blk, k_prefix, v_prefix, prefix_len, sel, active * c->cfg.n_kv_heads, false, s);
+      if (st != FB_OK) return st;
+    }
+    st = run_internal(c, q_blk, k_blk, v_blk, out, sel, reuse_now, s);
+    std::fill(c->host_valid.begin(), c->host_valid.end(), 1);
+  }
+  if (st != FB_OK) return st;
+  if (c->steps == 0) {
+    c->block_prefix = prefix_len;
+    c->block_policy = pa->policy;
+  }
+  c->steps += 1;
+  return ok();
+}
+
+fb_status fb_cache_read(const fb_cache* c, int32_t field, void* host_dst, size_t bytes, void* stream) {
+  if (!c) return fail(FB_E_ARG, "cache is null");
+  if (!host_dst) return fail(FB_E_ARG, "host_dst is null");
+  const int64_t nh = (int64_t)c->cfg.batch * c->cfg.n_q_heads;
+  const int64_t so = elems_per_slot(c->cfg), sl = rows_per_slot(c->cfg);
+  size_t want;
+  switch (field) {
+    case FB_FIELD_A_OUT: want = so * sizeof(float); break;
+    case FB_FIELD_L_OUT: want = sl * sizeof(float); break;
+    case FB_FIELD_SIM: want = nh * sizeof(float); break;
+    case FB_FIELD_REUSE:
+    case FB_FIELD_VALID: want = nh; break;
+    default: return fail(FB_E_ARG, "unknown field %d", field);
+  }
+  if (bytes != want) return fail(FB_E_ARG, "field %d needs %zu bytes, got %zu", field, want, bytes);
+  DeviceGuard g(c->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "set device");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronise");
+  if (field == FB_FIELD_A_OUT || field == FB_FIELD_L_OUT) {
+    std::vector<uint8_t> cur(nh);
+    e = hipMemcpy(cur.data(), c->cur, nh, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "copy");
+    const bool is_o = field == FB_FIELD_A_OUT;
+    const int64_t per_head = is_o ? (int64_t)c->cfg.block_size * c->cfg.head_dim : c->cfg.block_size;
+    const float* base = is_o ? c->slot_o : c->slot_l;
+    const int64_t slot_stride = is_o ? so : sl;
+    for (int64_t bh = 0; bh < nh; ++bh) {
+      e = hipMemcpy(static_cast<float*>(host_dst) + bh * per_head, base + cur[bh] * slot_stride + bh * per_head,
+                    per_head * sizeof(float), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "copy");
+    }
+    return ok();
+  }
+  const void* src = field == FB_FIELD_SIM ? (const void*)c->sim
+                    : field == FB_FIELD_VALID ? (const void*)c->valid
+                                              : (const void*)(c->reuse + ((c->steps + 1) & 1) * nh);
+  e = hipMemcpy(host_dst, src, want, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "copy");
+  return ok();
+}
+
+fb_status fb_cache_info(const fb_cache* c, size_t* device_bytes, int32_t* kv_splits) {
+  if (!c) return fail(FB_E_ARG, "cache is null");
+  if (device_bytes) *device_bytes = c->bytes;
+  if (kv_splits) *kv_splits = c->splits_cap;
+  return ok();
+}
+
+fb_status fb_profile_enable(fb_cache* c, int32_t enable) {
+  if (!c) return fail(FB_E_ARG, "cache is null");
+  c->prof = enable != 0;
+  return ok();
+}
+
+fb_status fb_profile_read(fb_cache* c, fb_profile_stats* out) {
+  if (!c || !out) return fail(FB_E_ARG, "null argument");
+  DeviceGuard g(c->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "set device");
+  for (auto& r : c->prof_recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "event timing");
+    c->prof_launches[r.kind] += 1;
+    c->prof_ms[r.kind] += ms;
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  c->prof_recs.clear();
+  for (int k = 0; k < FB_PROFILE_KINDS; ++k) {
+    out->launches[k] = c->prof_launches[k];
+    out->ms[k] = c->prof_ms[k];
+    c->prof_launches[k] = 0;
+    c->prof_ms[k] = 0.0;
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+"""Python binding of libfb.so (include/fb.h): argument marshalling only.
+
+Every step of the attention path runs in the library's HIP kernels; this
+module checks tensor dtypes, shapes, devices and contiguity, then passes raw
+device pointers and the current HIP stream through ctypes.  It raises
+``ImportError`` when the library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfb.so")
+
+FB_OK, FB_E_ARG, FB_E_SHAPE, FB_E_DTYPE, FB_E_STATE, FB_E_NOMEM, FB_E_HIP, FB_E_UNSUPPORTED = range(8)
+FB_F32, FB_BF16 = 0, 1
+POLICY_ALWAYS, POLICY_TAU, POLICY_GAMMA = 0, 1, 2
+FIELD_A_OUT, FIELD_L_OUT, FIELD_SIM, FIELD_REUSE, FIELD_VALID = range(5)
+PROFILE_KINDS = 8
+KIND_NAMES = ["external", "combine", "internal_merge", "decide", "reset"]
+
+STATUS_NAMES = {0: "FB_OK", 1: "FB_E_ARG", 2: "FB_E_SHAPE", 3: "FB_E_DTYPE", 4: "FB_E_STATE",
+                5: "FB_E_NOMEM", 6: "FB_E_HIP", 7: "FB_E_UNSUPPORTED"}
+
+EXPORTED = ["fb_cache_alloc", "fb_cache_free", "fb_cache_reset", "fb_external_attn",
+            "fb_internal_attn_merge", "fb_step", "fb_cache_read", "fb_cache_info",
+            "fb_profile_enable", "fb_profile_read", "fb_last_error"]
+
+
+class FBConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("max_prefix", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("kv_splits", ctypes.c_int32)]
+
+
+class FBPolicyArgs(ctypes.Structure):
+    _fields_ = [("policy", ctypes.c_int32), ("tau", ctypes.c_int32), ("gamma", ctypes.c_float),
+                ("n_updated", ctypes.POINTER(ctypes.c_int32))]
+
+
+class FBProfileStats(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64 * PROFILE_KINDS), ("ms", ctypes.c_double * PROFILE_KINDS)]
+
+
+class FBError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfb.so (once).  Raises ImportError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m cached_attention_fb_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32
+    lib.fb_cache_alloc.argtypes = [ctypes.POINTER(FBConfig), ctypes.POINTER(vp)]
+    lib.fb_cache_free.argtypes = [vp]
+    lib.fb_cache_reset.argtypes = [vp, vp]
+    lib.fb_external_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+    lib.fb_internal_attn_merge.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.fb_step.argtypes = [vp, ctypes.POINTER(FBPolicyArgs), vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.fb_cache_read.argtypes = [vp, i32, vp, ctypes.c_size_t, vp]
+    lib.fb_cache_info.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32)]
+    lib.fb_profile_enable.argtypes = [vp, i32]
+    lib.fb_profile_read.argtypes = [vp, ctypes.POINTER(FBProfileStats)]
+    for name in EXPORTED[:-1]:
+        getattr(lib, name).restype = st
+    lib.fb_last_error.argtypes = []
+    lib.fb_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(code: int) -> None:
+    if code != FB_OK:
+        raise FBError(code, load().fb_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+class Cache:
+    """One FlashBlock cache (fb_cache) and the entry points that use it."""
+
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, block_size: int,
+                 max_prefix: int, dtype: torch.dtype, softmax_scale: float = 0.0, kv_splits: int = 0):
+        self.lib = load()
+        self.dtype = dtype
+        self.cfg = FBConfig(batch, n_q_heads, n_kv_heads, head_dim, block_size, max_prefix,
+                            FB_F32 if dtype == torch.float32 else FB_BF16 if dtype == torch.bfloat16 else -1,
+                            softmax_scale, kv_splits)
+        h = ctypes.c_void_p()
+        _check(self.lib.fb_cache_alloc(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self.h = h
+
+    # -- shape checks (marshalling only) --------------------------------
+    def _t(self, t: torch.Tensor, shape: Sequence[int], name: str) -> int:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.dtype != self.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, the cache uses {self.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return t.data_ptr()
+
+    def _q(self, q, name="q_blk"):
+        c = self.cfg
+        return self._t(q, (c.batch, c.n_q_heads, c.block_size, c.head_dim), name)
+
+    def _kv_blk(self, t, name):
+        c = self.cfg
+        return self._t(t, (c.batch, c.n_kv_heads, c.block_size, c.head_dim), name)
+
+    def _kv_pre(self, t, name):
+        c = self.cfg
+        return self._t(t, (c.batch, c.n_kv_heads, c.max_prefix, c.head_dim), name)
+
+    # -- entry points ----------------------------------------------------
+    def reset(self, stream=None) -> None:
+        _check(self.lib.fb_cache_reset(self.h, _stream(stream)))
+
+    def external_attn(self, q, k_prefix, v_prefix, prefix_len: int, head_mask=None, stream=None) -> None:
+        mask = None
+        if head_mask is not None:
+            if head_mask.dtype != torch.uint8 or not head_mask.is_cuda or head_mask.numel() != self.cfg.batch * self.cfg.n_q_heads:
+                raise ValueError("head_mask must be a device uint8 tensor of B*Hq elements")
+            mask = head_mask.contiguous().data_ptr()
+        _check(self.lib.fb_external_attn(self.h, self._q(q), self._kv_pre(k_prefix, "k_prefix"),
+                                         self._kv_pre(v_prefix, "v_prefix"), int(prefix_len), mask,
+                                         _stream(stream)))
+
+    def internal_attn_merge(self, q, k_blk, v_blk, out, stream=None) -> None:
+        _check(self.lib.fb_internal_attn_merge(self.h, self._q(q), self._kv_blk(k_blk, "k_blk"),
+                                               self._kv_blk(v_blk, "v_blk"), self._q(out, "out"),
+                                               _stream(stream)))
+
+    def step(self, policy: int, q, k_blk, v_blk, k_prefix, v_prefix, prefix_len: int, out,
+             tau: int = 0, gamma: float = 0.0, n_updated=None, stream=None) -> None:
+        args = FBPolicyArgs(policy, tau, gamma, None)
+        keep = None
+        if n_updated is not None:
+            keep = np.ascontiguousarray(np.asarray(n_updated, dtype=np.int32).reshape(-1))
+            if keep.size != self.cfg.batch:
+                raise ValueError(f"n_updated needs {self.cfg.batch} entries")
+            args.n_updated = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        _check(self.lib.fb_step(self.h, ctypes.byref(args), self._q(q), self._kv_blk(k_blk, "k_blk"),
+                                self._kv_blk(v_blk, "v_blk"), self._kv_pre(k_prefix, "k_prefix"),
+                                self._kv_pre(v_prefix, "v_prefix"), int(prefix_len), self._q(out, "out"),
+                                _stream(stream)))
+
+    def read(self, field: int, stream=None) -> np.ndarray:
+        c = self.cfg
+        nh = (c.batch, c.n_q_heads)
+        shape, dt = {FIELD_A_OUT: (nh + (c.block_size, c.head_dim), np.float32),
+                     FIELD_L_OUT: (nh + (c.block_size,), np.float32),
+                     FIELD_SIM: (nh, np.float32), FIELD_REUSE: (nh, np.uint8),
+                     FIELD_VALID: (nh, np.uint8)}[field]
+        buf = np.empty(shape, dtype=dt)
+        _check(self.lib.fb_cache_read(self.h, field, buf.ctypes.data, buf.nbytes, _stream(stream)))
+        return buf
+
+    def info(self):
+        nb, ns = ctypes.c_size_t(), ctypes.c_int32()
+        _check(self.lib.fb_cache_info(self.h, ctypes.byref(nb), ctypes.byref(ns)))
+        return {"device_bytes": nb.value, "kv_splits": ns.value}
+
+    def profile_enable(self, on: bool = True) -> None:
+        _check(self.lib.fb_profile_enable(self.h, 1 if on else 0))
+
+    def profile_read(self):
+        st = FBProfileStats()
+        _check(self.lib.fb_profile_read(self.h, ctypes.byref(st)))
+        return {KIND_NAMES[k]: (st.launches[k], st.ms[k]) for k in range(len(KIND_NAMES))}
+
+    def close(self) -> None:
+        if getattr(self, "h", None):
+            self.lib.fb_cache_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

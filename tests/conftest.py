@@ -9,3 +9,21 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workload; minutes on the CPU")
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a device; on a machine without one they are skipped (the
+    CPU suite runs with -m "not gpu").  With a device present they always run,
+    and they fail loudly if the HIP library is not built."""
+    import pytest
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU in this environment")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)
