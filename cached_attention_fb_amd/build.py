@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfb.so")
-SOURCES = ["fb_kernels.hip", "fb_runtime.cpp"]
+SOURCES = ["fb_attn_bf16.hip", "fb_attn_f32.hip", "fb_aux.hip", "fb_runtime.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -18,6 +18,8 @@ def hipcc_command(out=LIB, extra=()):
     return [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             # keep fp32 arithmetic off the packed-fp32 VALU forms
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the softmax works on them without AGPR copies
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             *[os.path.join(CSRC, s) for s in SOURCES], *extra, "-o", out]
 

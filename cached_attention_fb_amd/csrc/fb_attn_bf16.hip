@@ -1,0 +1,345 @@
+// bf16 attention kernel for gfx950 (CDNA4).
+//
+// One workgroup = ROWW x KSPLIT wave64.  The ROWW row-waves own 32 packed
+// query rows each of one (sequence, kv head) group; with KSPLIT = 2 a second
+// set of ROWW waves takes the same rows and the other 32-key half of every
+// tile, so two independent waves share each SIMD and one's softmax overlaps
+// the other's MFMAs.  The two halves' (O, m, sum) are merged in LDS at the end.
+//
+// K/V 64-key tiles stream from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging) through a ring of kStages
+// buffers, so kStages-1 tiles are in flight per workgroup.  Each wave computes
+// S^T = K Q^T (K rows read with ds_read_b128) and O^T += V^T P^T, the V^T
+// operand coming from row-major LDS through the transposing
+// ds_read_b64_tr_b16.  The softmax runs in the log2 domain in fp32.
+//
+// LDS layout of one stage: K tile [64][D] then V tile [64][D], bf16, both
+// row-major in 16-byte chunks with an XOR swizzle chosen on the global side
+// (each lane of a DMA load writes a fixed LDS slot, so the lane picks which
+// global chunk to fetch):
+//   K: chunk c of key k at c ^ (k % (D/8))       (16 rows, one chunk column: all banks)
+//   V: chunk c of key k at c ^ (4(k % 4) % (D/8)) (4 rows x 64 B of a transposed read: all banks)
+#include <algorithm>
+
+#include "fb_device.h"
+
+namespace fbk {
+
+namespace {
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Transposed LDS reads (ds_read_b64_tr_b16) of the V^T operands of one 32-key
+// half C (k-steps 2C and 2C+1, every head-dim tile, both 4-key sub-halves),
+// waited for inside the same asm block so the results have landed when it
+// ends.  Written in asm because with the builtin the compiler waits for every
+// DMA load still in flight before each read, which would drain the tile
+// pipeline.  base[dt] = the lane's offset for head-dim tile dt; k-step ks,
+// sub-half hf sits (16ks + 8hf) rows further.  r[(kl*kDt + dt)*2 + hf].
+template <int D, int C>
+__device__ __forceinline__ void tr_read_half(u32x2 (&r)[D / 8], const uint32_t (&base)[D / 32]) {
+  constexpr int o00 = (32 * C + 0) * D * 2, o01 = (32 * C + 8) * D * 2;
+  constexpr int o10 = (32 * C + 16) * D * 2, o11 = (32 * C + 24) * D * 2;
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %2, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %4, %18 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %6, %19 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %10, %17 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %12, %18 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %13, %18 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(o00), "i"(o01), "i"(o10), "i"(o11)
+        : "memory");
+  } else if constexpr (D == 64) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(base[0]), "v"(base[1]), "i"(o00), "i"(o01), "i"(o10), "i"(o11)
+        : "memory");
+  }
+}
+
+template <int D, int WAVES>
+struct Pipe {
+  static constexpr int kCpr = D / 8;                             // 16-byte chunks per row
+  static constexpr int kTensorBytes = kKeyTile * D * 2;          // one K or V tile
+  static constexpr int kInstrPerTensor = kKeyTile * kCpr / 64;   // wave-wide 1 KB DMA loads
+  static constexpr int kLpt = 2 * kInstrPerTensor / WAVES;       // DMA loads per wave per tile
+  static constexpr int kStages = (2 * kLpt <= 63) ? 4 : 3;       // wait counts must fit vmcnt
+  static constexpr int kStageBytes = 2 * kTensorBytes;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static_assert(2 * kInstrPerTensor % WAVES == 0, "tile loads split evenly over the waves");
+};
+
+template <int D, int WAVES>
+__device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, const bf16* vb, int tile0,
+                                           int key_end, int wave, int lane) {
+  using P = Pipe<D, WAVES>;
+#pragma unroll
+  for (int j = 0; j < P::kLpt; ++j) {
+    const int idx = wave * P::kLpt + j;
+    const int tensor = idx / P::kInstrPerTensor;   // 0: K, 1: V (wave-uniform)
+    const int ii = idx % P::kInstrPerTensor;
+    const int pos = ii * 64 + lane;                 // 16-byte slot inside the tile
+    const int key = pos / P::kCpr, pc = pos % P::kCpr;
+    const int swz = tensor == 0 ? (key & (P::kCpr - 1)) : ((4 * key) & (P::kCpr - 4));
+    const int gk = min(tile0 + key, key_end - 1);   // rows past the end: any valid row (masked later)
+    const bf16* src = (tensor == 0 ? kb : vb) + (int64_t)gk * D + (pc ^ swz) * 8;
+    __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(stage + tensor * P::kTensorBytes + ii * 1024), 16, 0, 0);
+  }
+}
+
+// LDS bytes of the end-of-loop exchange between the two key halves.
+template <int D, int ROWW>
+constexpr int xch_bytes() { return ROWW * (16 * (D / 32) + 2) * 64 * 4; }
+
+template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT>
+__global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const AttnParams p) {
+  constexpr int WAVES = ROWW * KSPLIT;
+  constexpr int NH = 2 / KSPLIT;   // 32-key halves of a tile per wave
+  using P = Pipe<D, WAVES>;
+  constexpr int kDt = D / 32;
+  extern __shared__ char smem_raw[];
+  FB_LDS char* lds = (FB_LDS char*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rw = wave % ROWW, kh = wave / ROWW;
+  const int rl = lane & 31, hl = lane >> 5;
+  const AttnItem it = attn_item(p);
+  const int b = it.b, g = it.g, grp = p.hq / p.hkv;
+  if (MODE == kModePartial) {
+    bool any = false;
+    for (int i = 0; i < grp; ++i) any |= head_selected(p.sel, b, b * p.hq + g * grp + i);
+    if (!any) return;
+  }
+  const int key_begin = it.split * p.keys_per_split;
+  const int key_end = min(p.n_keys, key_begin + p.keys_per_split);
+  const int ntiles = key_end > key_begin ? (key_end - key_begin + kKeyTile - 1) / kKeyTile : 0;
+  const int row0 = it.rt * ROWW * 32 + rw * 32;
+  const int row = row0 + rl;
+  const bool row_ok = row < p.rows;
+  const bool wave_live = row0 < p.rows;
+  const int64_t grow = (int64_t)(b * p.hq + g * grp) * p.bs + row;
+  const int bh = b * p.hq + g * grp + (row_ok ? row / p.bs : 0);
+
+  const bf16* qg = reinterpret_cast<const bf16*>(p.q);
+  const bf16* kb = reinterpret_cast<const bf16*>(p.k) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
+  const bf16* vb = reinterpret_cast<const bf16*>(p.v) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
+
+  // Tile 0 first, then Q and the cached external part, then the other
+  // prologue tiles.
+  int issued = 0;
+  if (ntiles > 0) {
+    issue_tile<D, WAVES>(lds, kb, vb, key_begin, key_end, wave, lane);
+    issued = 1;
+  }
+  // Q^T as the B operand: lane (row, hl) holds Q[row][16t + 8hl .. +7].
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    qf[t] = row_ok ? *reinterpret_cast<const bf16x8*>(qg + grow * D + 16 * t + 8 * hl) : bf16x8{};
+  ExtPart<D> ext;
+  if constexpr (MODE == kModeMerge && PREFETCH_EXT) {
+    if (row_ok && kh == 0) ext.load(p, bh, grow, hl);
+  }
+  for (; issued < P::kStages - 1 && issued < ntiles; ++issued)
+    issue_tile<D, WAVES>(lds + issued * P::kStageBytes, kb, vb, key_begin + issued * kKeyTile, key_end, wave, lane);
+
+  f32x16 o[kDt];
+#pragma unroll
+  for (int i = 0; i < kDt; ++i) o[i] = f32x16{};
+  float m = -INFINITY, lsum = 0.0f;
+
+  // Per-lane byte offsets of the transposed V reads inside a V tile.  In a
+  // 16-lane group tg, lane 4j + q addresses 4 columns of key 4hl + j (plus
+  // 16ks + 8hf); the instruction hands lane i the column 16(tg%2) + i of the
+  // 4 keys, i.e. the A-operand layout of V^T for head-dim tile dt.
+  uint32_t tr_off[kDt];
+  {
+    const int tg = lane >> 4, tj = (lane & 15) >> 2, tq = lane & 3;
+    const int key = 4 * hl + tj;
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+      const int cl = 4 * dt + 2 * (tg & 1) + (tq >> 1);
+      const int pc = cl ^ ((4 * key) & (P::kCpr - 4));
+      tr_off[dt] = key * D * 2 + pc * 16 + (tq & 1) * 8;
+    }
+  }
+  // Per-lane byte offsets of the K reads (key rl of a 32-key half, 16-byte
+  // chunk 2t + hl); half c is 32c rows further.
+  uint32_t k_off[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) k_off[t] = rl * D * 2 + (((2 * t + hl) ^ (rl & (P::kCpr - 1))) * 16);
+
+  for (int t_i = 0; t_i < ntiles; ++t_i) {
+    const int after = issued - t_i - 1;   // tiles issued after this one, still in flight
+    if constexpr (P::kStages >= 4) {
+      if (after >= 2) wait_vmcnt<2 * P::kLpt>();
+      else if (after == 1) wait_vmcnt<P::kLpt>();
+      else wait_vmcnt<0>();
+    } else {
+      if (after >= 1) wait_vmcnt<P::kLpt>();
+      else wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();   // every wave's share of this tile landed; the oldest stage is free
+    if (issued < ntiles) {
+      issue_tile<D, WAVES>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, key_begin + issued * kKeyTile,
+                           key_end, wave, lane);
+      ++issued;
+    }
+    if (!wave_live) continue;
+    const int tile0 = key_begin + t_i * kKeyTile;
+    const FB_LDS char* ks = lds + (t_i % P::kStages) * P::kStageBytes;
+    const uint32_t vs_off = (uint32_t)(uintptr_t)(ks + P::kTensorBytes);
+
+    // S^T of this wave's key halves
+    f32x16 s[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) s[h] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int c = kh * NH + h;
+        const bf16x8 a = *reinterpret_cast<const FB_LDS bf16x8*>(ks + k_off[t] + c * 32 * D * 2);
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[h], 0, 0, 0);
+      }
+    }
+    // V^T operands of the same halves, read while the S MFMAs run
+    uint32_t base[kDt];
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) base[dt] = vs_off + tr_off[dt];
+    u32x2 vr[NH][D / 8];
+    if constexpr (NH == 2) {
+      tr_read_half<D, 0>(vr[0], base);
+      tr_read_half<D, 1>(vr[NH - 1], base);
+    } else {
+      if (kh == 0) tr_read_half<D, 0>(vr[0], base);
+      else tr_read_half<D, 1>(vr[0], base);
+    }
+    softmax_tile<kDt, NH>(s, o, m, lsum, tile0 + 32 * kh * NH, key_end, hl, p.scale_log2);
+
+    // O^T += V^T P^T.  k-step kl of a half takes keys 16kl + 8(i/4) + 4hl + i%4
+    // (i = 0..7) of that half from both operands.
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = (bf16)s[h][8 * kl + i];
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) {
+          const u32x2 lo = vr[h][(kl * kDt + dt) * 2], hi = vr[h][(kl * kDt + dt) * 2 + 1];
+          const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pb, o[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if constexpr (KSPLIT == 2) {
+    // Merge the two key halves of each row: the second wave set hands its
+    // (O, m, lane sum) to the first through LDS.  No DMA is in flight here
+    // (the last tile waited for vmcnt 0), so the ring can be reused.
+    constexpr int kRegs = 16 * kDt + 2;
+    FB_LDS float* xch = (FB_LDS float*)lds + rw * kRegs * 64 + lane;
+    __builtin_amdgcn_s_barrier();
+    if (kh == 1 && wave_live) {
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) xch[(dt * 16 + j) * 64] = o[dt][j];
+      }
+      xch[(16 * kDt) * 64] = m;
+      xch[(16 * kDt + 1) * 64] = lsum;
+    }
+    __builtin_amdgcn_s_barrier();
+    if (kh == 1) return;
+    if (wave_live) {
+      const float m2 = xch[(16 * kDt) * 64], l2 = xch[(16 * kDt + 1) * 64];
+      const float mt = fmaxf(m, m2);
+      const float a1 = m > -INFINITY ? fast_exp2(m - mt) : 0.0f;
+      const float a2 = m2 > -INFINITY ? fast_exp2(m2 - mt) : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[dt][j] = a1 * o[dt][j] + a2 * xch[(dt * 16 + j) * 64];
+      }
+      lsum = a1 * lsum + a2 * l2;
+      m = mt;
+    }
+  }
+
+  const float ltot = pair_sum(lsum);
+  if (!row_ok) return;
+  if constexpr (MODE == kModePartial) {
+    store_partial<D>(p, o, m, ltot, it.split, grow, hl);
+  } else {
+    if (p.reuse_rec != nullptr && hl == 0 && (row % p.bs) == 0) p.reuse_rec[bh] = head_selected(p.sel, b, bh) ? 0 : 1;
+    if constexpr (!PREFETCH_EXT) ext.load(p, bh, grow, hl);
+    merge_store<bf16, D>(p, o, m, ltot, ext, grow, hl);
+  }
+}
+
+template <int D, int ROWW, int KSPLIT, int MODE, bool PF>
+hipError_t launch_one(const AttnParams& p, hipStream_t s) {
+  using P = Pipe<D, ROWW * KSPLIT>;
+  const int blocks = p.batch * p.hkv * p.splits * p.row_tiles;
+  if (blocks == 0) return hipSuccess;
+  constexpr int kMaxLds = std::max(P::kLdsBytes, KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  // a workgroup never uses more ring stages than its key range has tiles
+  const int max_tiles = (p.keys_per_split + kKeyTile - 1) / kKeyTile;
+  int lds = std::max(1, std::min(P::kStages, max_tiles)) * P::kStageBytes;
+  if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
+  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF>), dim3(blocks), dim3(64 * ROWW * KSPLIT), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int D, int MODE, bool PF_SMALL>
+hipError_t launch_mode(const AttnParams& p, hipStream_t s) {
+  if (p.waves == 8 && p.ksplit == 1) return launch_one<D, 8, 1, MODE, false>(p, s);
+  if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false>(p, s);
+  return launch_one<D, 1, 1, MODE, PF_SMALL>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(int head_dim, int mode, const AttnParams& p, hipStream_t s) {
+  if (head_dim == 64)
+    return mode == kModePartial ? launch_mode<64, kModePartial, false>(p, s) : launch_mode<64, kModeMerge, true>(p, s);
+  return mode == kModePartial ? launch_mode<128, kModePartial, false>(p, s) : launch_mode<128, kModeMerge, true>(p, s);
+}
+
+}  // namespace fbk

@@ -1,0 +1,190 @@
+// Split combine, gamma decision and reset kernels (gfx950), and the attention
+// dispatcher.
+#include "fb_device.h"
+
+namespace fbk {
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Split combine (page §2's log-space rule over the prefix chunks):
+// A = sum_s e^{L_s - M} A_s / sum_s e^{L_s - M}, L = M + log sum, M = max_s L_s.
+// One wave per workgroup, D/4 lanes (one float4 column each) per row.  The
+// splits are folded in a fixed order, 8 at a time with all their loads in
+// flight, keeping a running max (an online form of the same sum).  Under
+// gamma it writes the other slot and sums <A_new, A_old>, |A_new|^2, |A_old|^2
+// over its rows for the similarity.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p) {
+  constexpr int kLpr = D / 4;
+  constexpr int kRows = kCombineThreads / kLpr;
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / p.row_chunks, ch = blockIdx.x % p.row_chunks;
+  const int b = bh / p.hq;
+  if (!head_selected(p.sel, b, bh)) return;
+  const int src = p.cur[bh];
+  const int dst = p.to_other_slot ? (src ^ 1) : src;
+  const bool sim_terms = p.to_other_slot && p.valid[bh] != 0;
+  const int c4 = tid % kLpr;
+  const int i = ch * kRows + tid / kLpr;
+  float dot = 0.0f, nn = 0.0f, no = 0.0f;
+  if (i < p.bs) {
+    const int64_t grow = (int64_t)bh * p.bs + i;
+    const float* lp = p.part_l + grow;
+    const float* ap = p.part_o + grow * D + 4 * c4;
+    float mx = -INFINITY, wsum = 0.0f;
+    f32x4 acc = {0, 0, 0, 0};
+    int s = 0;
+    for (; s + 8 <= p.splits; s += 8) {
+      float l[8];
+      f32x4 a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        l[u] = lp[(s + u) * p.part_l_stride];
+        a[u] = *reinterpret_cast<const f32x4*>(ap + (s + u) * p.part_o_stride);
+      }
+      float cm = l[0];
+#pragma unroll
+      for (int u = 1; u < 8; ++u) cm = fmaxf(cm, l[u]);
+      const float nm = fmaxf(mx, cm);
+      if (nm > -INFINITY) {
+        const float sc = fast_exp2((mx - nm) * kLog2e);
+        acc *= sc;
+        wsum *= sc;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float w = fast_exp2((l[u] - nm) * kLog2e);
+          wsum += w;
+          acc += w * a[u];
+        }
+        mx = nm;
+      }
+    }
+    for (; s < p.splits; ++s) {
+      const float l = lp[s * p.part_l_stride];
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ap + s * p.part_o_stride);
+      const float nm = fmaxf(mx, l);
+      if (nm > -INFINITY) {
+        const float sc = fast_exp2((mx - nm) * kLog2e);
+        const float w = fast_exp2((l - nm) * kLog2e);
+        acc = acc * sc + w * a;
+        wsum = wsum * sc + w;
+        mx = nm;
+      }
+    }
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    const f32x4 a_new = acc * inv;
+    const float lse = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
+    if (sim_terms) {
+      const f32x4 a_old = *reinterpret_cast<const f32x4*>(p.slot_o + src * p.slot_o_stride + grow * D + 4 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot += a_new[e] * a_old[e];
+        nn += a_new[e] * a_new[e];
+        no += a_old[e] * a_old[e];
+      }
+    }
+    *reinterpret_cast<f32x4*>(p.slot_o + dst * p.slot_o_stride + grow * D + 4 * c4) = a_new;
+    if (c4 == 0) p.slot_l[dst * p.slot_l_stride + grow] = lse;
+  }
+  if (sim_terms) {
+    dot = wave_sum(dot);
+    nn = wave_sum(nn);
+    no = wave_sum(no);
+    if (tid == 0) {
+      float* t = p.cos_part + ((int64_t)bh * p.row_chunks + ch) * 3;
+      t[0] = dot;
+      t[1] = nn;
+      t[2] = no;
+    }
+  }
+  if (!p.to_other_slot && ch == 0 && tid == 0) p.valid[bh] = 1;
+}
+
+// Gamma decisions, one workgroup per head: similarity of a recomputed head
+// from the combine's partial terms (summed in a fixed order), slot flip, and
+// the reuse decision of the next step (strict sim > gamma; NaN, i.e. no
+// similarity yet, never reuses).
+__global__ __launch_bounds__(kThreads) void decide_kernel(const DecideParams p) {
+  __shared__ float red[3][kThreads / 64];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const bool computed = p.reuse_now[bh] == 0;
+  const bool had_value = p.valid[bh] != 0;
+  __syncthreads();   // every thread has read the flags before thread 0 updates them
+  if (computed && had_value) {   // workgroup-uniform
+    float dot = 0.0f, nn = 0.0f, no = 0.0f;
+    for (int c = tid; c < p.row_chunks; c += kThreads) {
+      const float* t = p.cos_part + ((int64_t)bh * p.row_chunks + c) * 3;
+      dot += t[0];
+      nn += t[1];
+      no += t[2];
+    }
+    dot = wave_sum(dot);
+    nn = wave_sum(nn);
+    no = wave_sum(no);
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = dot;
+      red[1][tid >> 6] = nn;
+      red[2][tid >> 6] = no;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      dot = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+      nn = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+      no = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+      float sim;
+      if (nn == 0.0f || no == 0.0f) sim = (nn == 0.0f && no == 0.0f) ? 1.0f : 0.0f;
+      else sim = fminf(1.0f, fmaxf(-1.0f, dot / (sqrtf(nn) * sqrtf(no))));
+      p.sim[bh] = sim;
+    }
+  }
+  if (tid == 0) {
+    if (computed) {
+      p.cur[bh] ^= 1;
+      p.valid[bh] = 1;
+    }
+    const float s = p.sim[bh];
+    p.reuse_next[bh] = (p.valid[bh] && s > p.gamma) ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void reset_kernel(const ResetParams p) {
+  const int bh = blockIdx.x * kThreads + threadIdx.x;
+  if (bh >= p.n_heads) return;
+  p.cur[bh] = 0;
+  p.valid[bh] = 0;
+  p.reuse[bh] = 0;
+  p.reuse[p.n_heads + bh] = 0;
+  p.sim[bh] = __builtin_nanf("");
+}
+
+}  // namespace
+
+hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, hipStream_t s) {
+  return dtype == FB_BF16 ? launch_attn_bf16(head_dim, mode, p, s) : launch_attn_f32(head_dim, mode, p, s);
+}
+
+hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s) {
+  const int blocks = p.batch * p.hq * p.row_chunks;
+  if (blocks == 0) return hipSuccess;
+  if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(blocks), dim3(kCombineThreads), 0, s, p);
+  else hipLaunchKernelGGL(combine_kernel<128>, dim3(blocks), dim3(kCombineThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decide(const DecideParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(decide_kernel, dim3(p.n_heads), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(const ResetParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(reset_kernel, dim3((p.n_heads + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fbk

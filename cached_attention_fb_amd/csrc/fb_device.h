@@ -1,0 +1,210 @@
+// Device-side helpers shared by the gfx950 attention kernels.
+//
+// Page "Résumé Technique : FlashBlock", §2 "Mécanisme Central": attention of
+// the current block's queries is split into a block-external part (A_out,
+// L_out = log Z_out, over the committed prefix) and a block-internal part
+// (A_in, L_in, over the block itself), recombined in log space with
+// m = max(L_out, L_in).  The same log-space rule combines the partial results
+// of the prefix chunks that different workgroups attend (split-KV).
+//
+// Both attention kernels compute S^T = K Q^T and O^T += V^T P^T with 32x32
+// MFMAs.  In the transposed products lane l holds query row l % 32 in both
+// outputs (S^T: keys 8(j/4) + 4(l/32) + j%4 of a 32-key half in register j;
+// O^T: head-dim columns 32dt + 8(j/4) + 4(l/32) + j%4), so the online softmax
+// and the rescale of O stay inside the lane pair (l, l^32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fb_internal.h"
+
+namespace fbk {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FB_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum of a value over the lane pair (l, l^32) that shares a query row.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Map the hardware index so that consecutive logical work items share an XCD.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int q = total >> 3, r = total & 7, x = w & 7, j = w >> 3;
+  return x * q + min(x, r) + j;
+}
+
+__device__ __forceinline__ bool head_selected(const HeadSel& s, int b, int bh) {
+  if (!((s.seq_bits[b >> 5] >> (b & 31)) & 1u)) return false;
+  if (s.flags == nullptr) return true;
+  return (s.flags[bh] != 0) == (s.flags_select != 0);
+}
+
+// Work item of an attention workgroup: (sequence, kv head, key split, row tile).
+struct AttnItem {
+  int b, g, split, rt;
+};
+__device__ __forceinline__ AttnItem attn_item(const AttnParams& p) {
+  int w = xcd_remap(blockIdx.x, gridDim.x);
+  AttnItem it;
+  it.rt = w % p.row_tiles;
+  w /= p.row_tiles;
+  it.split = w % p.splits;
+  w /= p.splits;
+  it.g = w % p.hkv;
+  it.b = w / p.hkv;
+  return it;
+}
+
+// Online-softmax update of NH 32-key halves of S^T (raw scores) whose first
+// key is key0.  c = softmax scale * log2(e) > 0, so the max of the raw scores
+// gives the max of the scaled ones and P = exp2(c*s - m) takes one FMA per
+// score.  The running max m (log2 units) is only raised when a row's tile max
+// exceeds it by more than kRescale; until then P <= 2^kRescale, and the O/sum
+// rescale (rarely needed after the first tile) runs only when some row of the
+// wave raised its max.  The result is the same: the final normalisation
+// divides by the sum taken against the same m.  MASKED drops keys at or past
+// key_end (a row may then have seen no key yet: m stays -inf, P = 0).
+constexpr float kRescale = 8.0f;
+
+template <int kDt, int NH, bool MASKED>
+__device__ __forceinline__ void softmax_halves(f32x16 (&s)[NH], f32x16 (&o)[kDt], float& m, float& lsum,
+                                               int key0, int key_end, int hl, float c) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (MASKED) {
+        const int key = key0 + 32 * h + 8 * (j >> 2) + 4 * hl + (j & 3);
+        s[h][j] = key < key_end ? s[h][j] : -INFINITY;
+      }
+      mx = fmaxf(mx, s[h][j]);
+    }
+  }
+  mx = pair_max(mx) * c;
+  const bool raise = mx > m + kRescale;
+  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    const float m_new = raise ? mx : m;
+    const float alpha = fast_exp2(m - m_new);
+    m = m_new;
+    lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < kDt; ++i) o[i] *= alpha;
+  }
+  const float mref = MASKED ? (m > -INFINITY ? m : 0.0f) : m;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float e = fast_exp2(fmaf(s[h][j], c, -mref));
+      s[h][j] = e;
+      lsum += e;
+    }
+  }
+}
+
+template <int kDt, int NH>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[NH], f32x16 (&o)[kDt], float& m, float& lsum,
+                                             int key0, int key_end, int hl, float c) {
+  if (key0 + 32 * NH <= key_end) softmax_halves<kDt, NH, false>(s, o, m, lsum, key0, key_end, hl, c);
+  else softmax_halves<kDt, NH, true>(s, o, m, lsum, key0, key_end, hl, c);
+}
+
+// Epilogue of a partial (one key split): normalised A and natural-log L.
+template <int D>
+__device__ __forceinline__ void store_partial(const AttnParams& p, const f32x16 (&o)[D / 32], float m,
+                                              float ltot, int split, int64_t grow, int hl) {
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  const float lse = ltot > 0.0f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
+  float* od = p.part_o + split * p.part_o_stride + grow * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const f32x4 v4 = {o[dt][4 * gq] * inv, o[dt][4 * gq + 1] * inv, o[dt][4 * gq + 2] * inv,
+                        o[dt][4 * gq + 3] * inv};
+      *reinterpret_cast<f32x4*>(od + 32 * dt + 8 * gq + 4 * hl) = v4;
+    }
+  }
+  if (hl == 0) p.part_l[split * p.part_l_stride + grow] = lse;
+}
+
+// External part of one row for the merge: the head's cached A_out columns of
+// this lane (16 float4 for D=128) and L_out; an empty part when the head holds
+// nothing.
+template <int D>
+struct ExtPart {
+  f32x4 a[D / 8];
+  float l;
+  __device__ __forceinline__ void load(const AttnParams& p, int bh, int64_t grow, int hl) {
+    const bool has = p.valid[bh] != 0;
+    const int slot = p.cur[bh];
+    l = has ? p.slot_l[slot * p.slot_l_stride + grow] : -INFINITY;
+    const float* ao = p.slot_o + slot * p.slot_o_stride + grow * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        a[4 * dt + gq] = has ? *reinterpret_cast<const f32x4*>(ao + 32 * dt + 8 * gq + 4 * hl) : f32x4{0, 0, 0, 0};
+    }
+  }
+};
+
+// Epilogue of the block-internal attention: log-space merge with the external
+// part (page §2, A_full equation) and store in the output dtype.
+template <typename T, int D>
+__device__ __forceinline__ void merge_store(const AttnParams& p, const f32x16 (&o)[D / 32], float m, float ltot,
+                                            const ExtPart<D>& ext, int64_t grow, int hl) {
+  const float l_in = (m + log2f(ltot)) * kLn2;
+  const float mm = fmaxf(ext.l, l_in);
+  const float w_out = fast_exp2((ext.l - mm) * kLog2e);
+  const float w_in = fast_exp2((l_in - mm) * kLog2e);
+  const float inv_den = 1.0f / (w_out + w_in);
+  const float c_in = w_in / ltot * inv_den, c_out = w_out * inv_den;
+  T* od = reinterpret_cast<T*>(p.out) + grow * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d0 = 32 * dt + 8 * gq + 4 * hl;
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = c_out * ext.a[4 * dt + gq][e] + c_in * o[dt][4 * gq + e];
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 rb = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
+        *reinterpret_cast<bf16x4*>(od + d0) = rb;
+      } else {
+        *reinterpret_cast<f32x4*>(od + d0) = r;
+      }
+    }
+  }
+}
+
+// Launchers of the two attention kernel families.
+hipError_t launch_attn_f32(int head_dim, int mode, const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_bf16(int head_dim, int mode, const AttnParams& p, hipStream_t s);
+
+}  // namespace fbk

@@ -10,11 +10,13 @@
 
 namespace fbk {
 
-constexpr int kThreads = 256;     // 4 wave64 per workgroup
-constexpr int kRowTile = 128;     // packed query rows per attention workgroup (32 per wave)
+constexpr int kThreads = 256;     // threads of the fp32 attention and auxiliary workgroups
 constexpr int kKeyTile = 64;      // keys staged in LDS per iteration
-constexpr int kCombineRows = 32;  // rows of one head per combine workgroup
 constexpr int kMaxSplits = 64;
+
+// Combine workgroups are one wave; a row takes D/4 lanes (one float4 each).
+constexpr int kCombineThreads = 64;
+constexpr int combine_rows(int head_dim) { return 4 * kCombineThreads / head_dim; }
 
 // Which heads a launch works on.  A head (b, h) is selected when bit b of
 // `seq_bits` is set and, if `flags` is not null, (flags[b*Hq+h] != 0) equals
@@ -35,7 +37,9 @@ struct AttnParams {
   int64_t kv_cap;         // rows per (b, kv head) in k/v
   int32_t n_keys;         // keys 0..n_keys-1 are attended
   int32_t batch, hq, hkv, bs, rows;   // rows = (Hq/Hkv) * Bs
-  int32_t row_tiles;      // ceil(rows / kRowTile)
+  int32_t waves;          // wave64 per workgroup
+  int32_t ksplit;         // 1, or 2: two wave sets split every key tile (waves/ksplit own 32 rows each)
+  int32_t row_tiles;      // ceil(rows / (32 * waves / ksplit))
   int32_t splits;         // key ranges per group
   int32_t keys_per_split; // multiple of kKeyTile
   float scale_log2;       // softmax scale * log2(e)

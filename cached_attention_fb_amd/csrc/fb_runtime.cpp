@@ -63,7 +63,11 @@ struct fb_cache {
   int device = 0;
   int group = 1;         // Hq / Hkv
   int rows = 0;          // packed rows per (b, kv head) = group * Bs
-  int row_tiles = 0;
+  int ext_waves = 4;     // waves per external-attention workgroup
+  int ext_ksplit = 1;    // 2: two wave sets share the rows and split each key tile
+  int row_tiles = 0;     // external-attention row tiles per group
+  int int_waves = 4;     // waves per internal-attention workgroup
+  int int_ksplit = 1;
   int row_chunks = 0;    // combine workgroups per head
   int splits_cap = 1;    // splits the scratch is sized for
   float scale = 0.0f;
@@ -161,22 +165,25 @@ fbk::HeadSel all_heads(const fb_cache* c) {
   return h;
 }
 
-fbk::AttnParams attn_common(const fb_cache* c, const void* q) {
+fbk::AttnParams attn_common(const fb_cache* c, const void* q, int waves, int ksplit) {
   fbk::AttnParams p{};
+  p.waves = waves;
+  p.ksplit = ksplit;
+  const int rows_per_wg = 32 * waves / ksplit;
+  p.row_tiles = (c->rows + rows_per_wg - 1) / rows_per_wg;
   p.q = q;
   p.batch = c->cfg.batch;
   p.hq = c->cfg.n_q_heads;
   p.hkv = c->cfg.n_kv_heads;
   p.bs = c->cfg.block_size;
   p.rows = c->rows;
-  p.row_tiles = c->row_tiles;
   p.scale_log2 = c->scale * 1.4426950408889634f;
   return p;
 }
 
 fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* vp, int32_t n,
                        const fbk::HeadSel& sel, int active_groups, bool gamma, hipStream_t s) {
-  fbk::AttnParams p = attn_common(c, q);
+  fbk::AttnParams p = attn_common(c, q, c->ext_waves, c->ext_ksplit);
   p.k = kp;
   p.v = vp;
   p.kv_cap = c->cfg.max_prefix;
@@ -223,7 +230,7 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
 
 fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* vb, void* out,
                        const fbk::HeadSel& rec_sel, uint8_t* reuse_rec, hipStream_t s) {
-  fbk::AttnParams p = attn_common(c, q);
+  fbk::AttnParams p = attn_common(c, q, c->int_waves, c->int_ksplit);
   p.k = kb;
   p.v = vb;
   p.kv_cap = c->cfg.block_size;
@@ -299,8 +306,23 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
   c->device = dev;
   c->group = cfg->n_q_heads / cfg->n_kv_heads;
   c->rows = c->group * cfg->block_size;
-  c->row_tiles = (c->rows + fbk::kRowTile - 1) / fbk::kRowTile;
-  c->row_chunks = (cfg->block_size + fbk::kCombineRows - 1) / fbk::kCombineRows;
+  if (cfg->dtype == FB_BF16) {
+    // up to 128 rows: 4 row waves + 4 waves on the other key half of each
+    // tile; more rows: 8 row waves; 32 rows or fewer: a single wave
+    if (c->rows <= 32) c->ext_waves = 1, c->ext_ksplit = 1;
+    else if (c->rows <= 128) c->ext_waves = 8, c->ext_ksplit = 2;
+    else c->ext_waves = 8, c->ext_ksplit = 1;
+    // block-internal attention: one wave per 32 rows for small blocks, the
+    // split-key 8-wave shape for frame-sized ones
+    if (c->rows >= 512) c->int_waves = 8, c->int_ksplit = 2;
+    else c->int_waves = 1, c->int_ksplit = 1;
+  } else {
+    c->ext_waves = c->int_waves = 4;   // the fp32 kernel has a fixed shape
+  }
+  const int ext_rows_per_wg = 32 * c->ext_waves / c->ext_ksplit;
+  c->row_tiles = (c->rows + ext_rows_per_wg - 1) / ext_rows_per_wg;
+  const int crows = fbk::combine_rows(cfg->head_dim);
+  c->row_chunks = (cfg->block_size + crows - 1) / crows;
   c->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
   c->host_valid.assign(cfg->batch, 0);
   c->splits_cap = fbk::kMaxSplits;
@@ -410,13 +432,20 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   if (c->steps > 0 && pa->policy != c->block_policy)
     return fail(FB_E_STATE, "policy changed inside a block (reset first)");
   const int B = c->cfg.batch;
-  std::vector<uint8_t> recompute(B, 1);
+  // sequences whose heads recompute the external part (TAU decides per sequence)
+  fbk::HeadSel sel{};
+  int active = 0;
   if (pa->policy == FB_POLICY_TAU) {
     if (pa->tau < 0) return fail(FB_E_ARG, "tau %d is negative", pa->tau);
     if (!pa->n_updated) return fail(FB_E_ARG, "n_updated is null under the tau policy");
-    for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < B; ++b)
       if (pa->n_updated[b] < 0) return fail(FB_E_ARG, "n_updated[%d] = %d is negative", b, pa->n_updated[b]);
-      recompute[b] = (c->host_valid[b] && pa->n_updated[b] < pa->tau) ? 0 : 1;
+  }
+  for (int b = 0; b < B; ++b) {
+    const bool reuse = pa->policy == FB_POLICY_TAU && c->host_valid[b] && pa->n_updated[b] < pa->tau;
+    if (!reuse) {
+      sel.seq_bits[b >> 5] |= 1u << (b & 31);
+      ++active;
     }
   }
   if (pa->policy == FB_POLICY_GAMMA && !(pa->gamma == pa->gamma)) return fail(FB_E_ARG, "gamma is NaN");
@@ -428,7 +457,6 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   uint8_t* reuse_next = c->reuse + ((c->steps + 1) & 1) * nh;
 
   fb_status st = FB_OK;
-  fbk::HeadSel sel{};
   if (pa->policy == FB_POLICY_GAMMA) {
     sel = all_heads(c);
     sel.flags = reuse_now;
@@ -453,13 +481,6 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
     if (e != hipSuccess) return hip_fail(e, "decision launch");
     st = run_internal(c, q_blk, k_blk, v_blk, out, sel, nullptr, s);
   } else {
-    int active = 0;
-    for (int b = 0; b < B; ++b) {
-      if (recompute[b]) {
-        sel.seq_bits[b >> 5] |= 1u << (b & 31);
-        ++active;
-      }
-    }
     sel.flags = nullptr;
     sel.flags_select = 1;
     if (active > 0) {

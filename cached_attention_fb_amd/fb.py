@@ -170,6 +170,13 @@ class Cache:
                                 self._kv_pre(v_prefix, "v_prefix"), int(prefix_len), self._q(out, "out"),
                                 _stream(stream)))
 
+    def prepare(self, q, k_blk, v_blk, k_prefix, v_prefix, out) -> "PreparedStep":
+        """Check a set of step buffers once; the returned object calls fb_step
+        on them with only scalar marshalling (for loops over many steps)."""
+        return PreparedStep(self, self._q(q), self._kv_blk(k_blk, "k_blk"), self._kv_blk(v_blk, "v_blk"),
+                            self._kv_pre(k_prefix, "k_prefix"), self._kv_pre(v_prefix, "v_prefix"),
+                            self._q(out, "out"), (q, k_blk, v_blk, k_prefix, v_prefix, out))
+
     def read(self, field: int, stream=None) -> np.ndarray:
         c = self.cfg
         nh = (c.batch, c.n_q_heads)
@@ -204,3 +211,30 @@ class Cache:
             self.close()
         except Exception:
             pass
+
+
+class PreparedStep:
+    """fb_step on buffers checked once by Cache.prepare (they are kept alive
+    here).  n_updated is copied into a preallocated int32 array per call."""
+
+    def __init__(self, cache: Cache, q, kb, vb, kp, vp, out, keep):
+        self.cache, self.keep = cache, keep
+        self.ptrs = (q, kb, vb, kp, vp)
+        self.out = out
+        self.m = (ctypes.c_int32 * cache.cfg.batch)()
+        self.args = FBPolicyArgs(0, 0, 0.0, ctypes.cast(self.m, ctypes.POINTER(ctypes.c_int32)))
+        self.args_ref = ctypes.byref(self.args)
+        self.fn = cache.lib.fb_step
+
+    def __call__(self, policy: int, prefix_len: int, n_updated=None, tau: int = 0, gamma: float = 0.0,
+                 stream=None) -> None:
+        a = self.args
+        a.policy, a.tau, a.gamma = policy, tau, gamma
+        if n_updated is not None:
+            for i, v in enumerate(n_updated):
+                self.m[i] = int(v)
+        q, kb, vb, kp, vp = self.ptrs
+        code = self.fn(self.cache.h, self.args_ref, q, kb, vb, kp, vp, prefix_len, self.out,
+                       _stream(stream) if stream is None or not isinstance(stream, int) else stream)
+        if code != FB_OK:
+            _check(code)
