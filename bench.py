@@ -247,6 +247,19 @@ def cpu_baseline(w, budget_s: float):
             "us_per_layer_step": round(1e6 * block_s / len(blk.steps), 1)}
 
 
+def calibrate():
+    """A plain elementwise kernel of known traffic (reads 256 MiB, writes
+    256 MiB), run under the same counters as the attention kernels to scale
+    FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    x = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.mul(x, 2.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "torch.mul bf16, 256 MiB read + 256 MiB written per launch", "launches": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,7 +271,11 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0: automatic split-KV count")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true", help="only run the known-traffic reference kernel")
     args = ap.parse_args()
+    if args.calibrate:
+        calibrate()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
                                    "(the path would shard by (sequence, kv head) or by prefix chunk)"}))
