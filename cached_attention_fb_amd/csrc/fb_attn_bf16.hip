@@ -83,13 +83,30 @@ __device__ __forceinline__ void tr_read_half(u32x2 (&r)[D / 8], const uint32_t (
   }
 }
 
+// Wait until at most `after` tiles' DMA loads (kLpt per tile and wave) are
+// still in flight, i.e. this wave's share of the current tile has landed.
+// When after*kLpt does not fit the 6-bit counter, wait for fewer (safe).
+template <int kLpt, int kMaxAfter>
+__device__ __forceinline__ void wait_tile(int after) {
+  if constexpr (kMaxAfter >= 3 && 3 * kLpt <= 63) {
+    if (after >= 3) { wait_vmcnt<3 * kLpt>(); return; }
+  }
+  if constexpr (kMaxAfter >= 2 && 2 * kLpt <= 63) {
+    if (after >= 2) { wait_vmcnt<2 * kLpt>(); return; }
+  }
+  if constexpr (kLpt <= 63) {
+    if (after >= 1) { wait_vmcnt<kLpt>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
 template <int D, int WAVES>
 struct Pipe {
   static constexpr int kCpr = D / 8;                             // 16-byte chunks per row
   static constexpr int kTensorBytes = kKeyTile * D * 2;          // one K or V tile
   static constexpr int kInstrPerTensor = kKeyTile * kCpr / 64;   // wave-wide 1 KB DMA loads
   static constexpr int kLpt = 2 * kInstrPerTensor / WAVES;       // DMA loads per wave per tile
-  static constexpr int kStages = (2 * kLpt <= 63) ? 4 : 3;       // wait counts must fit vmcnt
+  static constexpr int kStages = 4;                              // 4 x 32 KB ring (D = 128)
   static constexpr int kStageBytes = 2 * kTensorBytes;
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static_assert(2 * kInstrPerTensor % WAVES == 0, "tile loads split evenly over the waves");
@@ -110,6 +127,38 @@ __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, c
     const int gk = min(tile0 + key, key_end - 1);   // rows past the end: any valid row (masked later)
     const bf16* src = (tensor == 0 ? kb : vb) + (int64_t)gk * D + (pc ^ swz) * 8;
     __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(stage + tensor * P::kTensorBytes + ii * 1024), 16, 0, 0);
+  }
+}
+
+// Epilogue of a partial through LDS: normalise, write this wave's 32 rows to
+// `st` (row-major, 16-byte chunk c of row r at c ^ (r % (D/4))), read them
+// back as whole rows and store D/4 lanes per row.  nrows = valid rows.
+template <int D>
+__device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f32x16 (&o)[D / 32], float m,
+                                                   float ltot, int split, int64_t grow0, int nrows,
+                                                   FB_LDS float* st, int lane) {
+  constexpr int kC = D / 4;                 // 16-byte chunks per fp32 row
+  constexpr int kRowsPerOp = 64 / kC;
+  const int rl = lane & 31, hl = lane >> 5;
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  const float lse = ltot > 0.0f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int c = 8 * dt + 2 * gq + hl;
+      const f32x4 v4 = {o[dt][4 * gq] * inv, o[dt][4 * gq + 1] * inv, o[dt][4 * gq + 2] * inv,
+                        o[dt][4 * gq + 3] * inv};
+      *reinterpret_cast<FB_LDS f32x4*>(st + rl * D + ((c ^ (rl & (kC - 1))) * 4)) = v4;
+    }
+  }
+  if (hl == 0 && rl < nrows) p.part_l[split * p.part_l_stride + grow0 + rl] = lse;
+  float* od = p.part_o + split * p.part_o_stride + grow0 * D;
+#pragma unroll
+  for (int k = 0; k < 32 / kRowsPerOp; ++k) {
+    const int r = k * kRowsPerOp + lane / kC, c = lane % kC;
+    const f32x4 v = *reinterpret_cast<const FB_LDS f32x4*>(st + r * D + ((c ^ (r & (kC - 1))) * 4));
+    if (r < nrows) *reinterpret_cast<f32x4*>(od + (int64_t)r * D + 4 * c) = v;
   }
 }
 
@@ -166,6 +215,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   if constexpr (MODE == kModeMerge && PREFETCH_EXT) {
     if (row_ok && kh == 0) ext.load(p, bh, grow, hl);
   }
+  // kStages-1 tiles ahead; each iteration refills the stage freed by the
+  // previous one.
   for (; issued < P::kStages - 1 && issued < ntiles; ++issued)
     issue_tile<D, WAVES>(lds + issued * P::kStageBytes, kb, vb, key_begin + issued * kKeyTile, key_end, wave, lane);
 
@@ -196,16 +247,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   for (int t = 0; t < D / 16; ++t) k_off[t] = rl * D * 2 + (((2 * t + hl) ^ (rl & (P::kCpr - 1))) * 16);
 
   for (int t_i = 0; t_i < ntiles; ++t_i) {
-    const int after = issued - t_i - 1;   // tiles issued after this one, still in flight
-    if constexpr (P::kStages >= 4) {
-      if (after >= 2) wait_vmcnt<2 * P::kLpt>();
-      else if (after == 1) wait_vmcnt<P::kLpt>();
-      else wait_vmcnt<0>();
-    } else {
-      if (after >= 1) wait_vmcnt<P::kLpt>();
-      else wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();   // every wave's share of this tile landed; the oldest stage is free
+    wait_tile<P::kLpt, P::kStages>(issued - t_i - 1);   // tiles issued after this one may stay in flight
+    __builtin_amdgcn_s_barrier();   // every wave's share of this tile landed; the previous stage is free
     if (issued < ntiles) {
       issue_tile<D, WAVES>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, key_begin + issued * kKeyTile,
                            key_end, wave, lane);
@@ -295,11 +338,24 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     }
   }
 
+  if constexpr (MODE == kModePartial) {
+    // Stage the wave's 32 normalised rows in its own LDS region (row-major,
+    // 16-byte chunks XOR-swizzled by row) and store whole rows: each store
+    // instruction then writes 1 KB of contiguous partials instead of 32
+    // scattered 32-byte pieces.  Waves use disjoint regions, so after the
+    // ring is released (barrier below, or the exchange above) no further
+    // synchronisation is needed.
+    if constexpr (KSPLIT == 1) __builtin_amdgcn_s_barrier();   // every wave finished reading the ring
+    if (!wave_live) return;
+    const float ltot = pair_sum(lsum);
+    constexpr int kRegionFloats = KSPLIT == 2 ? (16 * kDt + 2) * 64 : 32 * D;
+    store_partial_rows<D>(p, o, m, ltot, it.split, grow - rl, min(32, p.rows - row0),
+                          (FB_LDS float*)lds + rw * kRegionFloats, lane);
+    return;
+  }
   const float ltot = pair_sum(lsum);
   if (!row_ok) return;
-  if constexpr (MODE == kModePartial) {
-    store_partial<D>(p, o, m, ltot, it.split, grow, hl);
-  } else {
+  {
     if (p.reuse_rec != nullptr && hl == 0 && (row % p.bs) == 0) p.reuse_rec[bh] = head_selected(p.sel, b, bh) ? 0 : 1;
     if constexpr (!PREFETCH_EXT) ext.load(p, bh, grow, hl);
     merge_store<bf16, D>(p, o, m, ltot, ext, grow, hl);
@@ -311,7 +367,8 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   using P = Pipe<D, ROWW * KSPLIT>;
   const int blocks = p.batch * p.hkv * p.splits * p.row_tiles;
   if (blocks == 0) return hipSuccess;
-  constexpr int kMaxLds = std::max(P::kLdsBytes, KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0);
+  constexpr int kStageOut = MODE == kModePartial ? ROWW * 32 * D * 4 : 0;   // partial staging (KSPLIT 1)
+  constexpr int kMaxLds = std::max({P::kLdsBytes, KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF>,
@@ -323,6 +380,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   const int max_tiles = (p.keys_per_split + kKeyTile - 1) / kKeyTile;
   int lds = std::max(1, std::min(P::kStages, max_tiles)) * P::kStageBytes;
   if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
+  lds = std::max(lds, kStageOut);
   hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF>), dim3(blocks), dim3(64 * ROWW * KSPLIT), lds, s, p);
   return hipGetLastError();
 }

@@ -70,6 +70,7 @@ struct fb_cache {
   int int_ksplit = 1;
   int row_chunks = 0;    // combine workgroups per head
   int splits_cap = 1;    // splits the scratch is sized for
+  int n_cu = 256;        // compute units of the device
   float scale = 0.0f;
   size_t bytes = 0;
   // device memory
@@ -122,8 +123,11 @@ fb_status check_config(const fb_config* cfg) {
   return FB_OK;
 }
 
-// Number of prefix chunks: enough workgroups to fill 256 CUs, at least two
-// 64-key tiles per chunk, at most the scratch capacity.
+// Number of prefix chunks.  Each (group, row tile, chunk) is one workgroup
+// and each CU runs one at a time, so the time goes as
+// ceil(workgroups / CUs) x tiles per chunk.  Take the smallest chunk count
+// within 2 % of the best such time (more chunks mean more partial traffic),
+// with at least two 64-key tiles per chunk and at most the scratch capacity.
 int choose_splits(const fb_cache* c, int n_keys, int active_groups) {
   const int tiles = (n_keys + fbk::kKeyTile - 1) / fbk::kKeyTile;
   if (tiles <= 1) return 1;
@@ -132,8 +136,17 @@ int choose_splits(const fb_cache* c, int n_keys, int active_groups) {
     want = c->cfg.kv_splits;
   } else {
     const int base = std::max(1, active_groups * c->row_tiles);
-    want = (256 + base - 1) / base;
-    want = std::min(want, std::max(1, tiles / 2));
+    const int smax = std::max(1, std::min({tiles / 2, c->splits_cap, fbk::kMaxSplits}));
+    // makespan in tiles: rounds of workgroups x tiles per chunk, after
+    // rounding the chunks to whole tiles
+    auto span = [&](int sp) {
+      const int per = (tiles + sp - 1) / sp, eff = (tiles + per - 1) / per;
+      return (double)((base * eff + c->n_cu - 1) / c->n_cu) * per;
+    };
+    double best = 1e30;
+    for (int sp = 1; sp <= smax; ++sp) best = std::min(best, span(sp));
+    want = 1;
+    while (want < smax && span(want) > 1.02 * best) ++want;
   }
   want = std::max(1, std::min({want, tiles, c->splits_cap}));
   const int tiles_per = (tiles + want - 1) / want;
@@ -325,6 +338,11 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
   c->row_chunks = (cfg->block_size + crows - 1) / crows;
   c->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
   c->host_valid.assign(cfg->batch, 0);
+  {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+      c->n_cu = prop.multiProcessorCount;
+  }
   c->splits_cap = fbk::kMaxSplits;
   c->splits_cap = choose_splits(c, cfg->max_prefix, cfg->batch * cfg->n_kv_heads);
   if (cfg->kv_splits > 0) c->splits_cap = std::max(c->splits_cap, std::min(cfg->kv_splits, fbk::kMaxSplits));
