@@ -100,6 +100,66 @@ __device__ __forceinline__ void wait_tile(int after) {
   wait_vmcnt<0>();
 }
 
+// K^T operand fragments of one 32-key half: 16-byte chunk 2t + hl of the
+// lane's key row, t = 0..D/16-1, read with ds_read_b128 and waited for inside
+// the same asm block (one LDS wait per half instead of one per MFMA; asm for
+// the same reason as the transposed reads).  a[t] = row/chunk offset of the
+// lane in the stage, OFF = the half's offset (32 rows per half).
+template <int D, int OFF>
+__device__ __forceinline__ void k_read_half(u32x4 (&r)[D / 16], const uint32_t (&a)[D / 16]) {
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%16\n\t"
+        "ds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\t"
+        "ds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%16\n\t"
+        "ds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %14 offset:%16\n\t"
+        "ds_read_b128 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
+        : "memory");
+  } else if constexpr (D == 64) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\t"
+        "ds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\t"
+        "ds_read_b128 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+        : "memory");
+  }
+}
+
+// P = exp2(c*s - mref) of one S^T half, its contribution to the lane's row
+// sum, and the bf16 B operands of its two k-steps (registers j = 8kl .. 8kl+7).
+__device__ __forceinline__ void exp_half(f32x16& s, float mref, float c, float& lsum, bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float e = fast_exp2(fmaf(s[j], c, -mref));
+    lsum += e;
+    pb[j >> 3][j & 7] = (bf16)e;
+  }
+}
+
+// O^T += V^T P^T for one 32-key half: k-step kl takes keys 16kl + 8(i/4) +
+// 4hl + i%4 (i = 0..7) of the half from both operands.
+template <int kDt>
+__device__ __forceinline__ void pv_half(f32x16 (&o)[kDt], const u32x2 (&vr)[4 * kDt], const bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int kl = 0; kl < 2; ++kl) {
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+      const u32x2 lo = vr[(kl * kDt + dt) * 2], hi = vr[(kl * kDt + dt) * 2 + 1];
+      const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pb[kl], o[dt], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, int WAVES>
 struct Pipe {
   static constexpr int kCpr = D / 8;                             // 16-byte chunks per row
@@ -259,49 +319,84 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     const FB_LDS char* ks = lds + (t_i % P::kStages) * P::kStageBytes;
     const uint32_t vs_off = (uint32_t)(uintptr_t)(ks + P::kTensorBytes);
 
-    // S^T of this wave's key halves
+    // S^T, one 32-key half at a time: the half's K fragments in one batched
+    // LDS read, then its MFMA chain over the head dimension.
+    const uint32_t ks_off = (uint32_t)(uintptr_t)ks;
+    uint32_t ka[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) ka[t] = ks_off + k_off[t];
     f32x16 s[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) s[h] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const int c = kh * NH + h;
-        const bf16x8 a = *reinterpret_cast<const FB_LDS bf16x8*>(ks + k_off[t] + c * 32 * D * 2);
-        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[h], 0, 0, 0);
-      }
-    }
-    // V^T operands of the same halves, read while the S MFMAs run
-    uint32_t base[kDt];
-#pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) base[dt] = vs_off + tr_off[dt];
-    u32x2 vr[NH][D / 8];
-    if constexpr (NH == 2) {
-      tr_read_half<D, 0>(vr[0], base);
-      tr_read_half<D, 1>(vr[NH - 1], base);
-    } else {
-      if (kh == 0) tr_read_half<D, 0>(vr[0], base);
-      else tr_read_half<D, 1>(vr[0], base);
-    }
-    softmax_tile<kDt, NH>(s, o, m, lsum, tile0 + 32 * kh * NH, key_end, hl, p.scale_log2);
-
-    // O^T += V^T P^T.  k-step kl of a half takes keys 16kl + 8(i/4) + 4hl + i%4
-    // (i = 0..7) of that half from both operands.
+    // single-wave workgroups serve short blocks: skip a second key half that
+    // holds no key (wave-uniform; compiled only there, where registers allow)
+    constexpr bool kShortSkip = ROWW == 1 && NH == 2;
+    const int nh_live = (kShortSkip && tile0 + 32 >= key_end) ? 1 : NH;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
+      s[h] = f32x16{};
+      if (h >= nh_live) continue;
+      u32x4 kf[D / 16];
+      if (kh * NH + h == 0) k_read_half<D, 0>(kf, ka);
+      else k_read_half<D, 32 * D * 2>(kf, ka);
 #pragma unroll
-      for (int kl = 0; kl < 2; ++kl) {
-        bf16x8 pb;
+      for (int t = 0; t < D / 16; ++t)
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[h], 0, 0, 0);
+    }
+    // Ragged last tile: keys at or past key_end do not count.
+    const int key0 = tile0 + 32 * kh * NH;
+    if (key0 + 32 * NH > key_end) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = (bf16)s[h][8 * kl + i];
+      for (int h = 0; h < NH; ++h) {
 #pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) {
-          const u32x2 lo = vr[h][(kl * kDt + dt) * 2], hi = vr[h][(kl * kDt + dt) * 2 + 1];
-          const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pb, o[dt], 0, 0, 0);
-        }
+        for (int j = 0; j < 16; ++j)
+          if (key0 + 32 * h + 8 * (j >> 2) + 4 * hl + (j & 3) >= key_end) s[h][j] = -INFINITY;
       }
+    }
+    // Row max of this wave's keys (log2 units); the running max is raised only
+    // when it grows by more than 2^kRescale (see softmax_halves), so the O
+    // rescale below rarely runs after the first tile.
+    {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[h][j]);
+      }
+      mx = pair_max(mx) * p.scale_log2;
+      const bool raise = mx > m + kRescale;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? mx : m;
+        const float alpha = fast_exp2(m - m_new);
+        m = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < kDt; ++i) o[i] *= alpha;
+      }
+    }
+    const float mref = m > -INFINITY ? m : 0.0f;   // a row with no key yet (second half of a short block)
+    uint32_t vbase[kDt];
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) vbase[dt] = vs_off + tr_off[dt];
+    u32x2 vr[D / 8];
+    bf16x8 pb0[2];
+    if (kh * NH == 0) tr_read_half<D, 0>(vr, vbase);
+    else tr_read_half<D, 1>(vr, vbase);
+    exp_half(s[0], mref, p.scale_log2, lsum, pb0);
+    if (kShortSkip && nh_live == 1) {
+      pv_half<kDt>(o, vr, pb0);   // the second half holds no key (short block)
+    } else if constexpr (NH == 2) {
+      // half 1's exponentials are interleaved with half 0's PV MFMAs
+      bf16x8 pb1[2];
+      pv_half<kDt>(o, vr, pb0);
+      exp_half(s[NH - 1], mref, p.scale_log2, lsum, pb1);
+#pragma unroll
+      for (int i = 0; i < 2 * kDt; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then VALU
+      }
+      tr_read_half<D, 1>(vr, vbase);
+      pv_half<kDt>(o, vr, pb1);
+    } else {
+      pv_half<kDt>(o, vr, pb0);
     }
   }
 

@@ -15,7 +15,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Split combine (page §2's log-space rule over the prefix chunks):
 // A = sum_s e^{L_s - M} A_s / sum_s e^{L_s - M}, L = M + log sum, M = max_s L_s.
 // One wave per workgroup, D/4 lanes (one float4 column each) per row.  The
-// splits are folded in a fixed order, 8 at a time with all their loads in
+// splits are folded in a fixed order, 16 at a time with all their loads in
 // flight, keeping a running max (an online form of the same sum).  Under
 // gamma it writes the other slot and sums <A_new, A_old>, |A_new|^2, |A_old|^2
 // over its rows for the similarity.
@@ -40,24 +40,25 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     float mx = -INFINITY, wsum = 0.0f;
     f32x4 acc = {0, 0, 0, 0};
     int s = 0;
-    for (; s + 8 <= p.splits; s += 8) {
-      float l[8];
-      f32x4 a[8];
+    constexpr int kBatch = 16;   // splits whose loads are in flight together
+    for (; s + kBatch <= p.splits; s += kBatch) {
+      float l[kBatch];
+      f32x4 a[kBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kBatch; ++u) {
         l[u] = lp[(s + u) * p.part_l_stride];
         a[u] = *reinterpret_cast<const f32x4*>(ap + (s + u) * p.part_o_stride);
       }
       float cm = l[0];
 #pragma unroll
-      for (int u = 1; u < 8; ++u) cm = fmaxf(cm, l[u]);
+      for (int u = 1; u < kBatch; ++u) cm = fmaxf(cm, l[u]);
       const float nm = fmaxf(mx, cm);
       if (nm > -INFINITY) {
         const float sc = fast_exp2((mx - nm) * kLog2e);
         acc *= sc;
         wsum *= sc;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kBatch; ++u) {
           const float w = fast_exp2((l[u] - nm) * kLog2e);
           wsum += w;
           acc += w * a[u];
