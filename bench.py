@@ -1,24 +1,26 @@
 """Benchmark of the FlashBlock denoising-step attention on one MI355X.
 
 A bench step is one denoising step of the attention path (reuse decision,
-block-external attention for the heads that recompute, block-internal
-attention with the log-space merge) for every layer of a stack of
-independent attention layers of the workload's shape.  The timed steps walk
+block-external attention for the heads that recompute, split combine,
+block-internal attention with the log-space merge) for every layer of a stack
+of independent attention layers of the workload's shape.  The timed steps walk
 through the workload's seeded block of steps in order; every ``steps per
 block`` steps the caches are reset and the block starts again on the same
 prefix.  The stack holds enough layers that their prefix K/V exceed the
 256 MB MALL, as the layers of a model do, so every step streams its K/V from
 HBM without a cache flush in the timed region.
 
-Printed: one JSON line.  ``value`` is the effective KV bandwidth: the prefix
-K/V bytes a recompute-every-step (ALWAYS) run would read, divided by the time
-taken under the workload's reuse policy.  ``roofline`` reports the external
-attention kernel's algorithmic bytes per launch over its average launch
-duration (HIP events around each launch on its stream, in a profiled pass of
-the same steps under ALWAYS).  ``cpu_baseline`` times the float64 oracle on
-a bounded sample on the host cores.
+Printed: one JSON line for the headline workload (the dLLM layer, batch 1,
+32/8 heads, prefix 8192, block 32).  ``value`` is the effective KV bandwidth:
+the prefix K/V bytes a recompute-every-step (ALWAYS) run would read, divided by
+the time taken under the workload's reuse policy.  ``roofline`` reports the
+external attention kernel's algorithmic bytes per launch over its average
+launch duration (HIP events around each launch on its stream, in a profiled
+pass of the same steps under ALWAYS).  ``cpu_baseline`` times the float64
+oracle on the host cores.  ``workloads`` holds the same step and kernel
+figures, from fewer steps, for the other workloads.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dllm-8k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dllm-8k] [--no-extra]
 """
 from __future__ import annotations
 
@@ -36,10 +38,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "denoise-step attention µs & effective KV GB/s (% of HBM roofline), reuse vs full"
+UNIT = "GB/s (effective prefix-KV bandwidth under the reuse policy)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
+EXTRA = ["long-32k-b4", "max-128k", "video-1560x15600", "tiny-fp32"]
 
 
 def kernel_source_hash() -> str:
@@ -65,43 +69,55 @@ def algorithmic(w, n_prefix):
     return kv, kv + q + out, flops
 
 
-def run(args):
+def roofline(w, ext_us, alg_bytes, alg_flops):
+    """Roofline entry of the external kernel: the bound is whichever of HBM
+    bytes or MFMA flops takes longer at the published peaks."""
+    peak_f = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    if alg_flops / (peak_f * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9):
+        achieved = alg_flops / (ext_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_f, "unit": "TFLOP/s"}
+    else:
+        achieved = alg_bytes / (ext_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    return roof
+
+
+def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions=True):
+    """Time `steps` bench steps of workload `name` under its policy and under
+    ALWAYS, then a profiled ALWAYS pass (HIP events around every launch)."""
     import torch
     from cached_attention_fb_amd import fb
     from cached_attention_fb_amd import workload as wl
 
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    torch.cuda.set_device(0)
-    w = wl.workload(args.workload)
+    w = wl.workload(name)
     inp = wl.generate(w)
     blk = inp.blocks[0]
     S = len(blk.steps)
     n = w.prefix
     kv_bytes, alg_bytes, alg_flops = algorithmic(w, n)
-    layers = args.layers or max(1, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+    layers = layers or max(1, math.ceil(2.5 * MALL_BYTES / kv_bytes))
     dev = "cuda"
-    dt = w.torch_dtype
-    policy = {"tau": fb.POLICY_TAU, "gamma": fb.POLICY_GAMMA, "always": fb.POLICY_ALWAYS}[args.policy or w.policy]
+    policy_name = policy_name or w.policy
+    policy = {"tau": fb.POLICY_TAU, "gamma": fb.POLICY_GAMMA, "always": fb.POLICY_ALWAYS}[policy_name]
 
     # device inputs: per-layer prefix K/V and caches; step inputs shared by the layers
     kp0 = inp.k_prefix.to(dev)
     vp0 = inp.v_prefix.to(dev)
     prefixes = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(layers - 1)]
-    del inp
-    caches = [fb.Cache(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block, n, dt, kv_splits=args.splits)
-              for _ in range(layers)]
+    caches = [fb.Cache(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block, n, w.torch_dtype,
+                       kv_splits=splits) for _ in range(layers)]
     qs = [st.q.to(dev) for st in blk.steps]
     ks = [st.k.to(dev) for st in blk.steps]
     vs = [st.v.to(dev) for st in blk.steps]
     ms = [np.ascontiguousarray(st.n_updated, dtype=np.int32) for st in blk.steps]
+    del inp, blk
     outs = [torch.empty_like(qs[0]) for _ in range(layers)]
     # buffers checked once; each call then marshals only scalars
     prepared = [[c.prepare(qs[s], ks[s], vs[s], prefixes[li][0], prefixes[li][1], outs[li]) for s in range(S)]
                 for li, c in enumerate(caches)]
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
-
     state = {"s": 0}
 
     def step(pol):
@@ -113,37 +129,36 @@ def run(args):
             prepared[li][s](pol, n, m, w.tau, w.gamma, stream)
         state["s"] = (s + 1) % S
 
-    def timed(pol, k_steps):
+    def timed(pol):
         state["s"] = 0
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             step(pol)
         state["s"] = 0
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record()
-        for _ in range(k_steps):
+        for _ in range(steps):
             step(pol)
         e1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return wall, e0.elapsed_time(e1) / 1e3
+        return time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3
 
-    wall, gpu_s = timed(policy, args.steps)
-    wall_always, gpu_always = timed(fb.POLICY_ALWAYS, args.steps)
+    wall, gpu_s = timed(policy)
+    _, gpu_always = timed(fb.POLICY_ALWAYS)
 
-    # decisions of one block under the policy (from the caches' own record)
-    state["s"] = 0
     reuse_counts = []
-    for s in range(S):
-        step(policy)
-        reuse_counts.append(int(caches[0].read(fb.FIELD_REUSE).sum()))
+    if decisions:   # decisions of one block under the policy (the caches' own record)
+        state["s"] = 0
+        for _ in range(S):
+            step(policy)
+            reuse_counts.append(int(caches[0].read(fb.FIELD_REUSE).sum()))
 
-    # profiled pass: HIP events around every launch, ALWAYS policy (every step launches the external kernel)
+    # profiled pass under ALWAYS: every step launches the external kernel
     for c in caches:
         c.profile_enable(True)
     state["s"] = 0
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(fb.POLICY_ALWAYS)
     torch.cuda.synchronize()
     prof = {}
@@ -152,78 +167,56 @@ def run(args):
             a, b = prof.get(kname, (0, 0.0))
             prof[kname] = (a + cnt, b + tms)
         c.profile_enable(False)
-    ext_n, ext_ms = prof["external"]
-    ext_us = 1e3 * ext_ms / max(1, ext_n)
+    ext_us = 1e3 * prof["external"][1] / max(1, prof["external"][0])
     kernel_us = {k: round(1e3 * v[1] / v[0], 3) for k, v in prof.items() if v[0]}
-
-    bound_flops = alg_flops / (BF16_PEAK_TFLOPS * 1e12 if w.dtype == "bf16" else FP32_PEAK_TFLOPS * 1e12)
-    bound_bytes = alg_bytes / (HBM_PEAK_GBS * 1e9)
-    if bound_flops > bound_bytes:
-        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-        achieved = alg_flops / (ext_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s"}
-    else:
-        achieved = alg_bytes / (ext_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = "attn_kernel (external, split-KV partials)"
-    roof["avg_launch_us"] = round(ext_us, 3)
-    roof["algorithmic_bytes_per_launch"] = alg_bytes
-    roof["traffic"] = None
-    pmc = os.path.join(ROOT, "profiles", f"pmc_{w.name}.json")
-    if os.path.exists(pmc):
-        with open(pmc) as f:
-            rec = json.load(f)
-        if rec.get("kernel_source_hash") == kernel_source_hash():
-            roof["traffic"] = rec.get("hbm_bytes_per_launch")
-
-    per_step_s = gpu_s / args.steps
-    per_layer_step_us = 1e6 * per_step_s / layers
-    always_layer_step_us = 1e6 * gpu_always / args.steps / layers
-    eff_gbs = kv_bytes * layers * args.steps / gpu_s / 1e9
-
-    result = {
-        "metric": METRIC,
-        "value": round(eff_gbs, 1),
-        "unit": "GB/s (effective prefix-KV bandwidth under the reuse policy)",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(1e3 * per_step_s, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; random values of the workload's distributions)",
-        "config": {"workload": w.name, "shape": w.description, "policy": args.policy or w.policy,
-                   "tau": w.tau, "gamma": w.gamma, "layers": layers,
-                   "kv_bytes_per_layer": kv_bytes, "prefix": n},
-        "us_per_layer_step": round(per_layer_step_us, 3),
-        "always_us_per_layer_step": round(always_layer_step_us, 3),
-        "reuse_vs_full_speedup": round(always_layer_step_us / per_layer_step_us, 3),
-        "reused_heads_per_step": reuse_counts,
-        "wall_s": round(wall, 4),
-        "kernel_avg_us_always": kernel_us,
-        "roofline": roof,
-    }
     for c in caches:
         c.close()
-    return result, w
+    del prepared, caches, prefixes, kp0, vp0, qs, ks, vs, outs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    roof = roofline(w, ext_us, alg_bytes, alg_flops)
+    roof["kernel"] = ("attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel") + \
+        " (block-external, split-KV partials)"
+    roof["avg_launch_us"] = round(ext_us, 3)
+    roof["algorithmic_bytes_per_launch"] = alg_bytes
+    roof["algorithmic_flops_per_launch"] = alg_flops
+    return {
+        "w": w, "layers": layers, "kv_bytes": kv_bytes, "gpu_s": gpu_s, "wall_s": wall,
+        "per_layer_step_us": 1e6 * gpu_s / steps / layers,
+        "always_layer_step_us": 1e6 * gpu_always / steps / layers,
+        "eff_gbs": kv_bytes * layers * steps / gpu_s / 1e9, "reuse_counts": reuse_counts,
+        "kernel_us": kernel_us, "roofline": roof, "policy": policy_name,
+    }
 
 
-def cpu_baseline(w, budget_s: float):
-    """The float64 oracle on the host cores, on one block of the same workload
-    over a sample of heads; scaled to all heads."""
+def traffic_for(name):
+    """HBM bytes per external-attention launch from stored counters, while the
+    kernel sources are the ones they were taken on (else None)."""
+    pmc = os.path.join(ROOT, "profiles", f"pmc_{name}.json")
+    if not os.path.exists(pmc):
+        return None
+    with open(pmc) as f:
+        rec = json.load(f)
+    return rec.get("hbm_bytes_per_launch") if rec.get("kernel_source_hash") == kernel_source_hash() else None
+
+
+def cpu_baseline(name, budget_s: float):
+    """The float64 oracle on the host cores, on the same workload's block:
+    single-head runs in head order (starting over when every head is done)
+    until about budget_s seconds of work, scaled to all heads."""
     import oracle
     from threadpoolctl import threadpool_info
     from cached_attention_fb_amd import workload as wl
 
+    w = wl.workload(name)
     inp = wl.generate(w)
     blk = inp.blocks[0]
     kv_bytes, _, _ = algorithmic(w, w.prefix)
     heads = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)]
     done, t_total = 0, 0.0
-    for (b, h) in heads:
+    while t_total < budget_s:
+        b, h = heads[done % len(heads)]
         g = h // w.group
         steps = [oracle.StepData(wl.to_f64(s.q[b:b + 1, h:h + 1]), wl.to_f64(s.k[b:b + 1, g:g + 1]),
                                  wl.to_f64(s.v[b:b + 1, g:g + 1]), np.asarray(s.n_updated)[b:b + 1])
@@ -234,16 +227,13 @@ def cpu_baseline(w, budget_s: float):
         oracle.run_block(kp, vp, w.prefix, steps, w.policy, tau=w.tau, gamma=w.gamma)
         t_total += time.perf_counter() - t0
         done += 1
-        if t_total > budget_s:
-            break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     block_s = t_total * len(heads) / done
-    gbs = kv_bytes * len(blk.steps) / block_s / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s (effective prefix-KV bandwidth under the reuse policy)",
+    return {"value": round(kv_bytes * len(blk.steps) / block_s / 1e9, 4), "unit": UNIT,
             "cores": threads, "kind": "oracle",
-            "sample": f"one block of {len(blk.steps)} steps for {done} of {len(heads)} heads "
-                      f"({t_total:.1f} s), scaled to all heads; os.cpu_count()={os.cpu_count()}, "
-                      f"affinity={len(os.sched_getaffinity(0))}",
+            "sample": f"{done} single-head runs of one {len(blk.steps)}-step block of {name} "
+                      f"({len(heads)} heads per block, {t_total:.1f} s of oracle time), scaled to all heads; "
+                      f"os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}",
             "us_per_layer_step": round(1e6 * block_s / len(blk.steps), 1)}
 
 
@@ -269,8 +259,9 @@ def main():
     ap.add_argument("--policy", default=None, choices=[None, "tau", "gamma", "always"])
     ap.add_argument("--layers", type=int, default=0, help="0: enough layers to exceed 2.5x the MALL")
     ap.add_argument("--splits", type=int, default=0, help="0: automatic split-KV count")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate", action="store_true", help="only run the known-traffic reference kernel")
     args = ap.parse_args()
     if args.calibrate:
@@ -280,9 +271,59 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
                                    "(the path would shard by (sequence, kv head) or by prefix chunk)"}))
         raise SystemExit(2)
-    result, w = run(args)
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+
+    r = measure(args.workload, args.steps, args.warmup, args.policy, args.layers, args.splits)
+    w = r["w"]
+    roof = dict(r["roofline"])
+    roof["traffic"] = traffic_for(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(r["eff_gbs"], 1),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * r["gpu_s"] / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random values of the workload's distributions)",
+        "config": {"workload": w.name, "shape": w.description, "policy": r["policy"], "tau": w.tau,
+                   "gamma": w.gamma, "layers": r["layers"], "kv_bytes_per_layer": r["kv_bytes"],
+                   "prefix": w.prefix},
+        "us_per_layer_step": round(r["per_layer_step_us"], 3),
+        "always_us_per_layer_step": round(r["always_layer_step_us"], 3),
+        "reuse_vs_full_speedup": round(r["always_layer_step_us"] / r["per_layer_step_us"], 3),
+        "reused_heads_per_step": r["reuse_counts"],
+        "wall_s": round(r["wall_s"], 4),
+        "kernel_avg_us_always": r["kernel_us"],
+        "roofline": roof,
+    }
+    if not args.no_extra:
+        from cached_attention_fb_amd import workload as wl
+        extra = {}
+        for name in EXTRA:
+            if name == args.workload:
+                continue
+            S = wl.workload(name).steps
+            e = measure(name, 2 * S, S, decisions=False)
+            rf = e["roofline"]
+            extra[name] = {"policy": e["policy"], "layers": e["layers"], "steps": 2 * S,
+                           "us_per_layer_step": round(e["per_layer_step_us"], 2),
+                           "always_us_per_layer_step": round(e["always_layer_step_us"], 2),
+                           "reuse_vs_full_speedup": round(e["always_layer_step_us"] / e["per_layer_step_us"], 3),
+                           "effective_kv_gbs": round(e["eff_gbs"], 1),
+                           "external": {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                                           "avg_launch_us")},
+                           "kernel_avg_us_always": e["kernel_us"]}
+        result["workloads"] = extra
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 
