@@ -137,12 +137,14 @@ __device__ __forceinline__ void k_read_half(u32x4 (&r)[D / 16], const uint32_t (
 // P = exp2(c*s - mref) of one S^T half, its contribution to the lane's row
 // sum, and the bf16 B operands of its two k-steps (registers j = 8kl .. 8kl+7).
 __device__ __forceinline__ void exp_half(f32x16& s, float mref, float c, float& lsum, bf16x8 (&pb)[2]) {
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four short sum chains instead of one long one
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const float e = fast_exp2(fmaf(s[j], c, -mref));
-    lsum += e;
+    part[j & 3] += e;
     pb[j >> 3][j & 7] = (bf16)e;
   }
+  lsum += (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // O^T += V^T P^T for one 32-key half: k-step kl takes keys 16kl + 8(i/4) +
@@ -170,6 +172,15 @@ struct Pipe {
   static constexpr int kStageBytes = 2 * kTensorBytes;
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static_assert(2 * kInstrPerTensor % WAVES == 0, "tile loads split evenly over the waves");
+  // Ring stages a workgroup uses (never more than its key range has tiles).
+  __host__ __device__ static int ring_stages(int keys_per_split) {
+    const int t = (keys_per_split + kKeyTile - 1) / kKeyTile;
+    return t < 1 ? 1 : (t < kStages ? t : kStages);
+  }
+  // Q staging (ROWW x 32 rows x D, read once before the first tile): in ring
+  // stages 2-3 when the ring is full (those are first filled after Q has
+  // been read), else past the ring.
+  __host__ __device__ static int q_offset(int ring) { return ring == kStages ? 2 * kStageBytes : ring * kStageBytes; }
 };
 
 template <int D, int WAVES>
@@ -187,6 +198,20 @@ __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, c
     const int gk = min(tile0 + key, key_end - 1);   // rows past the end: any valid row (masked later)
     const bf16* src = (tensor == 0 ? kb : vb) + (int64_t)gk * D + (pc ^ swz) * 8;
     __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(stage + tensor * P::kTensorBytes + ii * 1024), 16, 0, 0);
+  }
+}
+
+// The wave's 32 query rows into LDS ([32][D], the K tile layout: 16-byte
+// chunk c of row r at c ^ (r % (D/8))), so that they are read like a K half.
+// Rows at or past rows_left repeat the last valid row.
+template <int D>
+__device__ __forceinline__ void issue_q(FB_LDS char* dst, const bf16* q_rows, int rows_left, int lane) {
+  constexpr int kCpr = D / 8;
+#pragma unroll
+  for (int j = 0; j < 32 * kCpr / 64; ++j) {
+    const int pos = j * 64 + lane, r = pos / kCpr, pc = pos % kCpr;
+    const bf16* src = q_rows + (int64_t)min(r, rows_left - 1) * D + (pc ^ (r & (kCpr - 1))) * 8;
+    __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(dst + j * 1024), 16, 0, 0);
   }
 }
 
@@ -259,26 +284,50 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   const bf16* kb = reinterpret_cast<const bf16*>(p.k) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
   const bf16* vb = reinterpret_cast<const bf16*>(p.v) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
 
-  // Tile 0 first, then Q and the cached external part, then the other
-  // prologue tiles.
-  int issued = 0;
-  if (ntiles > 0) {
+  // Prologue loads, none waiting on another: the merge's head flags, then Q
+  // and the first two tiles (more would only queue behind them in the memory
+  // system while the first is awaited), all three through the LDS DMA path.
+  // Q goes through LDS rather than straight into registers because the
+  // compiler cannot order register loads against the DMA loads and would
+  // drain the whole ring before every MFMA that reads Q.
+  ExtPart<D> ext;
+  const bool ext_lane = MODE == kModeMerge && row_ok && kh == 0;
+  if (ext_lane) ext.load_state(p, bh);
+  FB_LDS char* q_lds = lds + P::q_offset(P::ring_stages(p.keys_per_split)) + rw * 32 * D * 2;
+  if (kh == 0 && wave_live) issue_q<D>(q_lds, qg + (grow - rl) * D, p.rows - row0, lane);
+  int issued;
+  if (ntiles >= 2) {
+    issue_tile<D, WAVES>(lds, kb, vb, key_begin, key_end, wave, lane);
+    issue_tile<D, WAVES>(lds + P::kStageBytes, kb, vb, key_begin + kKeyTile, key_end, wave, lane);
+    issued = 2;
+    wait_vmcnt<P::kLpt>();   // tile 0 (and everything issued before it) landed
+  } else if (ntiles == 1) {
     issue_tile<D, WAVES>(lds, kb, vb, key_begin, key_end, wave, lane);
     issued = 1;
+    wait_vmcnt<0>();
+  } else {
+    issued = 0;
+    wait_vmcnt<0>();
   }
+  __builtin_amdgcn_s_barrier();   // every wave's share of tile 0 (and Q) landed
   // Q^T as the B operand: lane (row, hl) holds Q[row][16t + 8hl .. +7].
   bf16x8 qf[D / 16];
+  {
+    uint32_t qa[D / 16];
+    const uint32_t q0 = (uint32_t)(uintptr_t)q_lds;
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    qf[t] = row_ok ? *reinterpret_cast<const bf16x8*>(qg + grow * D + 16 * t + 8 * hl) : bf16x8{};
-  ExtPart<D> ext;
-  if constexpr (MODE == kModeMerge && PREFETCH_EXT) {
-    if (row_ok && kh == 0) ext.load(p, bh, grow, hl);
+    for (int t = 0; t < D / 16; ++t) qa[t] = q0 + rl * D * 2 + (((2 * t + hl) ^ (rl & (P::kCpr - 1))) * 16);
+    u32x4 qr[D / 16];
+    k_read_half<D, 0>(qr, qa);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) qf[t] = __builtin_bit_cast(bf16x8, qr[t]);
   }
-  // kStages-1 tiles ahead; each iteration refills the stage freed by the
-  // previous one.
-  for (; issued < P::kStages - 1 && issued < ntiles; ++issued)
-    issue_tile<D, WAVES>(lds + issued * P::kStageBytes, kb, vb, key_begin + issued * kKeyTile, key_end, wave, lane);
+  // When Q sits in ring stages 2-3, every wave must have read it before the
+  // first refill writes there.
+  if (P::ring_stages(p.keys_per_split) == P::kStages) __builtin_amdgcn_s_barrier();
+  if constexpr (MODE == kModeMerge && PREFETCH_EXT) {
+    if (ext_lane) ext.load_data(p, grow, hl);   // in flight while the tiles are processed
+  }
 
   f32x16 o[kDt];
 #pragma unroll
@@ -306,98 +355,100 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) k_off[t] = rl * D * 2 + (((2 * t + hl) ^ (rl & (P::kCpr - 1))) * 16);
 
+  // Single-wave workgroups serve short blocks: a second key half that holds
+  // no key is skipped (wave-uniform; compiled only there, where registers allow).
+  constexpr bool kShortSkip = ROWW == 1 && NH == 2;
+  const uint32_t lds_off = (uint32_t)(uintptr_t)lds;
   for (int t_i = 0; t_i < ntiles; ++t_i) {
-    wait_tile<P::kLpt, P::kStages>(issued - t_i - 1);   // tiles issued after this one may stay in flight
-    __builtin_amdgcn_s_barrier();   // every wave's share of this tile landed; the previous stage is free
-    if (issued < ntiles) {
+    if (t_i > 0) {
+      wait_tile<P::kLpt, P::kStages>(issued - t_i - 1);   // tiles issued after this one may stay in flight
+      __builtin_amdgcn_s_barrier();   // every wave's share landed; all waves finished tile t_i-1
+    }
+    if (wave_live) {
+      const int tile0 = key_begin + t_i * kKeyTile;
+      const uint32_t ks_off = lds_off + (t_i % P::kStages) * P::kStageBytes;
+      const uint32_t vs_off = ks_off + P::kTensorBytes;
+      // S^T, one 32-key half at a time: the half's K fragments in one batched
+      // LDS read, then its MFMA chain over the head dimension.
+      uint32_t ka[D / 16];
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) ka[t] = ks_off + k_off[t];
+      f32x16 s[NH];
+      const int nh_live = (kShortSkip && tile0 + 32 >= key_end) ? 1 : NH;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        s[h] = f32x16{};
+        if (h >= nh_live) continue;
+        u32x4 kf[D / 16];
+        if (kh * NH + h == 0) k_read_half<D, 0>(kf, ka);
+        else k_read_half<D, 32 * D * 2>(kf, ka);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[h], 0, 0, 0);
+      }
+      // Ragged last tile: keys at or past key_end do not count.
+      const int key0 = tile0 + 32 * kh * NH;
+      if (key0 + 32 * NH > key_end) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (key0 + 32 * h + 8 * (j >> 2) + 4 * hl + (j & 3) >= key_end) s[h][j] = -INFINITY;
+        }
+      }
+      // Row max of this wave's keys (log2 units); the running max is raised
+      // only when it grows by more than 2^kRescale (see softmax_halves), so
+      // the O rescale below rarely runs after the first tile.
+      {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[h][j]);
+        }
+        mx = pair_max(mx) * p.scale_log2;
+        const bool raise = mx > m + kRescale;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float m_new = raise ? mx : m;
+          const float alpha = fast_exp2(m - m_new);
+          m = m_new;
+          lsum *= alpha;
+#pragma unroll
+          for (int i = 0; i < kDt; ++i) o[i] *= alpha;
+        }
+      }
+      const float mref = m > -INFINITY ? m : 0.0f;   // a row with no key yet (second half of a short block)
+      uint32_t vbase[kDt];
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) vbase[dt] = vs_off + tr_off[dt];
+      u32x2 vr[D / 8];
+      bf16x8 pb0[2];
+      if (kh * NH == 0) tr_read_half<D, 0>(vr, vbase);
+      else tr_read_half<D, 1>(vr, vbase);
+      exp_half(s[0], mref, p.scale_log2, lsum, pb0);
+      if (kShortSkip && nh_live == 1) {
+        pv_half<kDt>(o, vr, pb0);   // the second half holds no key (short block)
+      } else if constexpr (NH == 2) {
+        // half 1's exponentials are interleaved with half 0's PV MFMAs
+        bf16x8 pb1[2];
+        pv_half<kDt>(o, vr, pb0);
+        exp_half(s[NH - 1], mref, p.scale_log2, lsum, pb1);
+#pragma unroll
+        for (int i = 0; i < 2 * kDt; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then VALU
+        }
+        tr_read_half<D, 1>(vr, vbase);
+        pv_half<kDt>(o, vr, pb1);
+      } else {
+        pv_half<kDt>(o, vr, pb0);
+      }
+    }
+    // Refill after the compute, so that a stalled issue does not delay it:
+    // the stage of tile t_i-1 is free (every wave passed the barrier above).
+    for (; issued < ntiles && issued <= t_i + P::kStages - 1; ++issued)
       issue_tile<D, WAVES>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, key_begin + issued * kKeyTile,
                            key_end, wave, lane);
-      ++issued;
-    }
-    if (!wave_live) continue;
-    const int tile0 = key_begin + t_i * kKeyTile;
-    const FB_LDS char* ks = lds + (t_i % P::kStages) * P::kStageBytes;
-    const uint32_t vs_off = (uint32_t)(uintptr_t)(ks + P::kTensorBytes);
-
-    // S^T, one 32-key half at a time: the half's K fragments in one batched
-    // LDS read, then its MFMA chain over the head dimension.
-    const uint32_t ks_off = (uint32_t)(uintptr_t)ks;
-    uint32_t ka[D / 16];
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) ka[t] = ks_off + k_off[t];
-    f32x16 s[NH];
-    // single-wave workgroups serve short blocks: skip a second key half that
-    // holds no key (wave-uniform; compiled only there, where registers allow)
-    constexpr bool kShortSkip = ROWW == 1 && NH == 2;
-    const int nh_live = (kShortSkip && tile0 + 32 >= key_end) ? 1 : NH;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      s[h] = f32x16{};
-      if (h >= nh_live) continue;
-      u32x4 kf[D / 16];
-      if (kh * NH + h == 0) k_read_half<D, 0>(kf, ka);
-      else k_read_half<D, 32 * D * 2>(kf, ka);
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t)
-        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[h], 0, 0, 0);
-    }
-    // Ragged last tile: keys at or past key_end do not count.
-    const int key0 = tile0 + 32 * kh * NH;
-    if (key0 + 32 * NH > key_end) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (key0 + 32 * h + 8 * (j >> 2) + 4 * hl + (j & 3) >= key_end) s[h][j] = -INFINITY;
-      }
-    }
-    // Row max of this wave's keys (log2 units); the running max is raised only
-    // when it grows by more than 2^kRescale (see softmax_halves), so the O
-    // rescale below rarely runs after the first tile.
-    {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[h][j]);
-      }
-      mx = pair_max(mx) * p.scale_log2;
-      const bool raise = mx > m + kRescale;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = raise ? mx : m;
-        const float alpha = fast_exp2(m - m_new);
-        m = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int i = 0; i < kDt; ++i) o[i] *= alpha;
-      }
-    }
-    const float mref = m > -INFINITY ? m : 0.0f;   // a row with no key yet (second half of a short block)
-    uint32_t vbase[kDt];
-#pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) vbase[dt] = vs_off + tr_off[dt];
-    u32x2 vr[D / 8];
-    bf16x8 pb0[2];
-    if (kh * NH == 0) tr_read_half<D, 0>(vr, vbase);
-    else tr_read_half<D, 1>(vr, vbase);
-    exp_half(s[0], mref, p.scale_log2, lsum, pb0);
-    if (kShortSkip && nh_live == 1) {
-      pv_half<kDt>(o, vr, pb0);   // the second half holds no key (short block)
-    } else if constexpr (NH == 2) {
-      // half 1's exponentials are interleaved with half 0's PV MFMAs
-      bf16x8 pb1[2];
-      pv_half<kDt>(o, vr, pb0);
-      exp_half(s[NH - 1], mref, p.scale_log2, lsum, pb1);
-#pragma unroll
-      for (int i = 0; i < 2 * kDt; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then VALU
-      }
-      tr_read_half<D, 1>(vr, vbase);
-      pv_half<kDt>(o, vr, pb1);
-    } else {
-      pv_half<kDt>(o, vr, pb0);
-    }
   }
 
   if constexpr (KSPLIT == 2) {
@@ -452,7 +503,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   if (!row_ok) return;
   {
     if (p.reuse_rec != nullptr && hl == 0 && (row % p.bs) == 0) p.reuse_rec[bh] = head_selected(p.sel, b, bh) ? 0 : 1;
-    if constexpr (!PREFETCH_EXT) ext.load(p, bh, grow, hl);
+    if constexpr (!PREFETCH_EXT) ext.load_data(p, grow, hl);
     merge_store<bf16, D>(p, o, m, ltot, ext, grow, hl);
   }
 }
@@ -463,7 +514,9 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   const int blocks = p.batch * p.hkv * p.splits * p.row_tiles;
   if (blocks == 0) return hipSuccess;
   constexpr int kStageOut = MODE == kModePartial ? ROWW * 32 * D * 4 : 0;   // partial staging (KSPLIT 1)
-  constexpr int kMaxLds = std::max({P::kLdsBytes, KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
+  constexpr int kQBytes = ROWW * 32 * D * 2;
+  constexpr int kMaxLds = std::max({P::kLdsBytes, (P::kStages - 1) * P::kStageBytes + kQBytes,
+                                    KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF>,
@@ -472,8 +525,8 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
     attr_set = true;
   }
   // a workgroup never uses more ring stages than its key range has tiles
-  const int max_tiles = (p.keys_per_split + kKeyTile - 1) / kKeyTile;
-  int lds = std::max(1, std::min(P::kStages, max_tiles)) * P::kStageBytes;
+  const int ring = P::ring_stages(p.keys_per_split);
+  int lds = std::max(ring * P::kStageBytes, P::q_offset(ring) + kQBytes);
   if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
   lds = std::max(lds, kStageOut);
   hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF>), dim3(blocks), dim3(64 * ROWW * KSPLIT), lds, s, p);

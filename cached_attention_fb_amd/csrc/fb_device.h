@@ -154,22 +154,32 @@ __device__ __forceinline__ void store_partial(const AttnParams& p, const f32x16 
 
 // External part of one row for the merge: the head's cached A_out columns of
 // this lane (16 float4 for D=128) and L_out; an empty part when the head holds
-// nothing.
+// nothing.  Loaded in two steps so that no load waits on another early in a
+// kernel: load_state reads the head's flags (which slot is current, whether it
+// holds a value), load_data then reads that slot unconditionally (the slots
+// are always allocated) and `has` is applied only at the merge.
 template <int D>
 struct ExtPart {
   f32x4 a[D / 8];
   float l;
-  __device__ __forceinline__ void load(const AttnParams& p, int bh, int64_t grow, int hl) {
-    const bool has = p.valid[bh] != 0;
-    const int slot = p.cur[bh];
-    l = has ? p.slot_l[slot * p.slot_l_stride + grow] : -INFINITY;
+  int slot;
+  bool has;
+  __device__ __forceinline__ void load_state(const AttnParams& p, int bh) {
+    has = p.valid[bh] != 0;
+    slot = p.cur[bh];
+  }
+  __device__ __forceinline__ void load_data(const AttnParams& p, int64_t grow, int hl) {
+    l = p.slot_l[slot * p.slot_l_stride + grow];
     const float* ao = p.slot_o + slot * p.slot_o_stride + grow * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq)
-        a[4 * dt + gq] = has ? *reinterpret_cast<const f32x4*>(ao + 32 * dt + 8 * gq + 4 * hl) : f32x4{0, 0, 0, 0};
+      for (int gq = 0; gq < 4; ++gq) a[4 * dt + gq] = *reinterpret_cast<const f32x4*>(ao + 32 * dt + 8 * gq + 4 * hl);
     }
+  }
+  __device__ __forceinline__ void load(const AttnParams& p, int bh, int64_t grow, int hl) {
+    load_state(p, bh);
+    load_data(p, grow, hl);
   }
 };
 
@@ -179,8 +189,9 @@ template <typename T, int D>
 __device__ __forceinline__ void merge_store(const AttnParams& p, const f32x16 (&o)[D / 32], float m, float ltot,
                                             const ExtPart<D>& ext, int64_t grow, int hl) {
   const float l_in = (m + log2f(ltot)) * kLn2;
-  const float mm = fmaxf(ext.l, l_in);
-  const float w_out = fast_exp2((ext.l - mm) * kLog2e);
+  const float l_out = ext.has ? ext.l : -INFINITY;
+  const float mm = fmaxf(l_out, l_in);
+  const float w_out = fast_exp2((l_out - mm) * kLog2e);
   const float w_in = fast_exp2((l_in - mm) * kLog2e);
   const float inv_den = 1.0f / (w_out + w_in);
   const float c_in = w_in / ltot * inv_den, c_out = w_out * inv_den;
@@ -192,7 +203,10 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, const f32x16 (&
       const int d0 = 32 * dt + 8 * gq + 4 * hl;
       f32x4 r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = c_out * ext.a[4 * dt + gq][e] + c_in * o[dt][4 * gq + e];
+      for (int e = 0; e < 4; ++e) {
+        const float a_out = ext.has ? ext.a[4 * dt + gq][e] : 0.0f;   // an empty slot may hold anything
+        r[e] = c_out * a_out + c_in * o[dt][4 * gq + e];
+      }
       if constexpr (sizeof(T) == 2) {
         bf16x4 rb = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
         *reinterpret_cast<bf16x4*>(od + d0) = rb;
