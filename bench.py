@@ -148,11 +148,32 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
     _, gpu_always = timed(fb.POLICY_ALWAYS)
 
     reuse_counts = []
+    step_full_us = step_reuse_us = None
     if decisions:   # decisions of one block under the policy (the caches' own record)
         state["s"] = 0
         for _ in range(S):
             step(policy)
             reuse_counts.append(int(caches[0].read(fb.FIELD_REUSE).sum()))
+        # per-step times (HIP events around each step of all layers), split into
+        # steps where some head recomputes ("full") and steps where all reuse
+        nh = w.batch * w.n_q_heads
+        state["s"] = 0
+        for _ in range(S):
+            step(policy)
+        state["s"] = 0
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record()
+        for i in range(steps):
+            step(policy)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        full, reuse = [], []
+        for i in range(steps):
+            us = 1e3 * evs[i].elapsed_time(evs[i + 1]) / layers
+            (reuse if reuse_counts[i % S] == nh else full).append(us)
+        step_full_us = float(np.median(full)) if full else None
+        step_reuse_us = float(np.median(reuse)) if reuse else None
 
     # profiled pass under ALWAYS: every step launches the external kernel
     for c in caches:
@@ -187,6 +208,7 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
         "always_layer_step_us": 1e6 * gpu_always / steps / layers,
         "eff_gbs": kv_bytes * layers * steps / gpu_s / 1e9, "reuse_counts": reuse_counts,
         "kernel_us": kernel_us, "roofline": roof, "policy": policy_name,
+        "step_full_us": step_full_us, "step_reuse_us": step_reuse_us,
     }
 
 
@@ -276,6 +298,10 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
 
+    # the largest prefix one layer's K/V can take in the free device memory
+    from cached_attention_fb_amd import workload as wl
+    w0 = wl.workload(args.workload)
+    capacity = int(torch.cuda.mem_get_info()[0] // (2 * w0.batch * w0.n_kv_heads * w0.head_dim * w0.elem_bytes))
     r = measure(args.workload, args.steps, args.warmup, args.policy, args.layers, args.splits)
     w = r["w"]
     roof = dict(r["roofline"])
@@ -300,12 +326,15 @@ def main():
         "always_us_per_layer_step": round(r["always_layer_step_us"], 3),
         "reuse_vs_full_speedup": round(r["always_layer_step_us"] / r["per_layer_step_us"], 3),
         "reused_heads_per_step": r["reuse_counts"],
+        "step_us_median": {"full": None if r["step_full_us"] is None else round(r["step_full_us"], 3),
+                           "all_reuse": None if r["step_reuse_us"] is None else round(r["step_reuse_us"], 3)},
+        "ext_plus_combine_us": round(r["kernel_us"].get("external", 0.0) + r["kernel_us"].get("combine", 0.0), 3),
+        "capacity_prefix_tokens_per_layer": capacity,
         "wall_s": round(r["wall_s"], 4),
         "kernel_avg_us_always": r["kernel_us"],
         "roofline": roof,
     }
     if not args.no_extra:
-        from cached_attention_fb_amd import workload as wl
         extra = {}
         for name in EXTRA:
             if name == args.workload:
