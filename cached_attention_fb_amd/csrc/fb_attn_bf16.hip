@@ -263,15 +263,10 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rw = wave % ROWW, kh = wave / ROWW;
   const int rl = lane & 31, hl = lane >> 5;
-  const AttnItem it = attn_item(p);
+  const AttnItem it = attn_item(p, MODE == kModePartial);
+  if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
   const int b = it.b, g = it.g, grp = p.hq / p.hkv;
-  if (MODE == kModePartial) {
-    bool any = false;
-    for (int i = 0; i < grp; ++i) any |= head_selected(p.sel, b, b * p.hq + g * grp + i);
-    if (!any) return;
-  }
-  const int key_begin = it.split * p.keys_per_split;
-  const int key_end = min(p.n_keys, key_begin + p.keys_per_split);
+  const int key_begin = it.key_begin, key_end = it.key_end;
   const int ntiles = key_end > key_begin ? (key_end - key_begin + kKeyTile - 1) / kKeyTile : 0;
   const int row0 = it.rt * ROWW * 32 + rw * 32;
   const int row = row0 + rl;
@@ -511,7 +506,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
 template <int D, int ROWW, int KSPLIT, int MODE, bool PF>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   using P = Pipe<D, ROWW * KSPLIT>;
-  const int blocks = p.batch * p.hkv * p.splits * p.row_tiles;
+  const int blocks = p.grid > 0 ? p.grid : p.batch * p.hkv * p.splits * p.row_tiles;
   if (blocks == 0) return hipSuccess;
   constexpr int kStageOut = MODE == kModePartial ? ROWW * 32 * D * 4 : 0;   // partial staging (KSPLIT 1)
   constexpr int kQBytes = ROWW * 32 * D * 2;

@@ -46,15 +46,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = lane & 31, hl = lane >> 5;
-  const AttnItem it = attn_item(p);
+  const AttnItem it = attn_item(p, MODE == kModePartial);
+  if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
   const int b = it.b, g = it.g, grp = p.hq / p.hkv;
-  if (MODE == kModePartial) {
-    bool any = false;
-    for (int i = 0; i < grp; ++i) any |= head_selected(p.sel, b, b * p.hq + g * grp + i);
-    if (!any) return;
-  }
-  const int key_begin = it.split * p.keys_per_split;
-  const int key_end = min(p.n_keys, key_begin + p.keys_per_split);
+  const int key_begin = it.key_begin, key_end = it.key_end;
   const int row0 = it.rt * kF32Waves * 32 + wave * 32;
   const int row = row0 + rl;
   const bool row_ok = row < p.rows;
@@ -119,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
 
 template <int D>
 hipError_t launch_d(int mode, const AttnParams& p, hipStream_t s) {
-  const int blocks = p.batch * p.hkv * p.splits * p.row_tiles;
+  const int blocks = p.grid > 0 ? p.grid : p.batch * p.hkv * p.splits * p.row_tiles;
   if (blocks == 0) return hipSuccess;
   if (mode == kModePartial)
     hipLaunchKernelGGL((attn_f32_kernel<D, kModePartial>), dim3(blocks), dim3(kThreads), 0, s, p);

@@ -27,6 +27,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
   const int bh = blockIdx.x / p.row_chunks, ch = blockIdx.x % p.row_chunks;
   const int b = bh / p.hq;
   if (!head_selected(p.sel, b, bh)) return;
+  int splits = p.splits;
+  if (p.dyn.groups > 0) {   // the external launch's device plan
+    const int n = __builtin_popcountll(active_groups(p.sel, p.dyn.groups, p.hq, p.hkv));
+    splits = p.dyn.splits[n];
+  }
   const int src = p.cur[bh];
   const int dst = p.to_other_slot ? (src ^ 1) : src;
   const bool sim_terms = p.to_other_slot && p.valid[bh] != 0;
@@ -41,7 +46,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     f32x4 acc = {0, 0, 0, 0};
     int s = 0;
     constexpr int kBatch = 16;   // splits whose loads are in flight together
-    for (; s + kBatch <= p.splits; s += kBatch) {
+    for (; s + kBatch <= splits; s += kBatch) {
       float l[kBatch];
       f32x4 a[kBatch];
 #pragma unroll
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
         mx = nm;
       }
     }
-    for (; s < p.splits; ++s) {
+    for (; s < splits; ++s) {
       const float l = lp[s * p.part_l_stride];
       const f32x4 a = *reinterpret_cast<const f32x4*>(ap + s * p.part_o_stride);
       const float nm = fmaxf(mx, l);

@@ -62,19 +62,68 @@ __device__ __forceinline__ bool head_selected(const HeadSel& s, int b, int bh) {
   return (s.flags[bh] != 0) == (s.flags_select != 0);
 }
 
-// Work item of an attention workgroup: (sequence, kv head, key split, row tile).
+// Groups (sequence, kv head) with at least one selected query head, as a bit
+// mask over the group index b*Hkv + g (groups <= 64), computed by every wave
+// from the head flags; and the number of splits the device plan gives them.
+__device__ __forceinline__ uint64_t active_groups(const HeadSel& sel, int groups, int hq, int hkv) {
+  const int lane = threadIdx.x & 63, grp = hq / hkv;
+  bool act = false;
+  if (lane < groups) {
+    const int b = lane / hkv, g = lane % hkv;
+    for (int i = 0; i < grp; ++i) act |= head_selected(sel, b, b * hq + g * grp + i);
+  }
+  return __builtin_amdgcn_ballot_w64(act);
+}
+
+// Work item of an attention workgroup: (sequence, kv head, key split, row
+// tile) and its key range.  Static plan: the grid enumerates every group,
+// groups without a selected head exit.  Device plan: the grid enumerates the
+// active groups only, with the split count chosen for their number.
 struct AttnItem {
   int b, g, split, rt;
+  int key_begin, key_end;
+  bool ok;
 };
-__device__ __forceinline__ AttnItem attn_item(const AttnParams& p) {
-  int w = xcd_remap(blockIdx.x, gridDim.x);
+__device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial) {
   AttnItem it;
-  it.rt = w % p.row_tiles;
-  w /= p.row_tiles;
-  it.split = w % p.splits;
-  w /= p.splits;
-  it.g = w % p.hkv;
-  it.b = w / p.hkv;
+  int kps = p.keys_per_split;
+  if (partial && p.dyn.groups > 0) {
+    const uint64_t mask = active_groups(p.sel, p.dyn.groups, p.hq, p.hkv);
+    const int n = __builtin_popcountll(mask);
+    const int splits = n > 0 ? p.dyn.splits[n] : 1;
+    const int items = n * p.row_tiles * splits;
+    it.ok = (int)blockIdx.x < items;
+    if (!it.ok) return it;
+    int w = xcd_remap(blockIdx.x, items);
+    it.rt = w % p.row_tiles;
+    w /= p.row_tiles;
+    it.split = w % splits;
+    int rank = w / splits;   // the rank-th active group
+    uint64_t m = mask;
+    for (; rank > 0; --rank) m &= m - 1;
+    const int group = __builtin_ctzll(m);
+    it.b = group / p.hkv;
+    it.g = group % p.hkv;
+    const int tiles = (p.n_keys + kKeyTile - 1) / kKeyTile;
+    kps = ((tiles + splits - 1) / splits) * kKeyTile;
+  } else {
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    it.rt = w % p.row_tiles;
+    w /= p.row_tiles;
+    it.split = w % p.splits;
+    w /= p.splits;
+    it.g = w % p.hkv;
+    it.b = w / p.hkv;
+    it.ok = true;
+    if (partial) {
+      const int grp = p.hq / p.hkv;
+      bool any = false;
+      for (int i = 0; i < grp; ++i) any |= head_selected(p.sel, it.b, it.b * p.hq + it.g * grp + i);
+      it.ok = any;
+    }
+  }
+  it.key_begin = it.split * kps;
+  it.key_end = min(p.n_keys, it.key_begin + kps);
   return it;
 }
 

@@ -27,6 +27,17 @@ struct HeadSel {
   int32_t flags_select;
 };
 
+// Split plan chosen on the device (per-head decisions made on the device,
+// gamma): with n of the (sequence, kv head) groups holding a selected head,
+// their work is cut into splits[n] key ranges each, so that fewer active
+// groups get more, shorter ranges and the launch keeps the chip busy.
+// groups = 0: off (the host's static plan applies).
+constexpr int kDynMaxGroups = 64;
+struct DynPlan {
+  int32_t groups;                        // B*Hkv when on
+  uint8_t splits[kDynMaxGroups + 1];     // splits[n], n = 1..groups
+};
+
 // Attention of packed query rows over one key range.  The G = Hq/Hkv query
 // heads of kv head g are contiguous in [B][Hq][Bs][D], so the G*Bs rows of a
 // (b, g) group form one contiguous [G*Bs][D] matrix ("packed rows").
@@ -40,10 +51,12 @@ struct AttnParams {
   int32_t waves;          // wave64 per workgroup
   int32_t ksplit;         // 1, or 2: two wave sets split every key tile (waves/ksplit own 32 rows each)
   int32_t row_tiles;      // ceil(rows / (32 * waves / ksplit))
+  int32_t grid;           // workgroups; 0: batch * hkv * splits * row_tiles
   int32_t splits;         // key ranges per group
-  int32_t keys_per_split; // multiple of kKeyTile
+  int32_t keys_per_split; // multiple of kKeyTile; with a device plan, the longest range it may pick
   float scale_log2;       // softmax scale * log2(e)
   HeadSel sel;
+  DynPlan dyn;            // partial mode only
   // partial epilogue: normalised A and natural-log L per split
   float* part_o;          // [splits][B][Hq][Bs][D]
   float* part_l;          // [splits][B][Hq][Bs]
@@ -62,8 +75,9 @@ struct CombineParams {
   const float* part_o;
   const float* part_l;
   int64_t part_o_stride, part_l_stride;
-  int32_t splits, batch, hq, bs, row_chunks;
+  int32_t splits, batch, hq, hkv, bs, row_chunks;
   HeadSel sel;
+  DynPlan dyn;            // the external launch's plan (split count from the same active groups)
   float* slot_o;
   float* slot_l;
   int64_t slot_o_stride, slot_l_stride;

@@ -70,6 +70,12 @@ struct fb_cache {
   int int_ksplit = 1;
   int row_chunks = 0;    // combine workgroups per head
   int splits_cap = 1;    // splits the scratch is sized for
+  // device split plan for per-head decisions made on the device (gamma),
+  // for the prefix length it was made for
+  fbk::DynPlan dyn{};
+  int32_t dyn_keys = -1;
+  int dyn_grid = 0;      // workgroups of the largest item count over the plan
+  int dyn_kps = 0;       // longest key range of the plan
   int n_cu = 256;        // compute units of the device
   float scale = 0.0f;
   size_t bytes = 0;
@@ -178,6 +184,29 @@ fbk::HeadSel all_heads(const fb_cache* c) {
   return h;
 }
 
+// Device split plan for up to kDynMaxGroups groups: for n active groups, the
+// split count the host would choose for n groups (makespan rule).  The
+// scratch allows at most max(static choice, kDynSplitCap) splits.
+constexpr int kDynSplitCap = 16;
+bool dyn_possible(const fb_cache* c) { return c->cfg.batch * c->cfg.n_kv_heads <= fbk::kDynMaxGroups; }
+void plan_dyn(fb_cache* c, int n_keys) {
+  if (c->dyn_keys == n_keys) return;
+  const int groups = c->cfg.batch * c->cfg.n_kv_heads;
+  const int tiles = (n_keys + fbk::kKeyTile - 1) / fbk::kKeyTile;
+  c->dyn.groups = groups;
+  c->dyn.splits[0] = 1;
+  c->dyn_grid = 0;
+  int min_splits = fbk::kMaxSplits;
+  for (int n = 1; n <= groups; ++n) {
+    const int sp = choose_splits(c, n_keys, n);
+    c->dyn.splits[n] = (uint8_t)sp;
+    c->dyn_grid = std::max(c->dyn_grid, n * c->row_tiles * sp);
+    min_splits = std::min(min_splits, sp);
+  }
+  c->dyn_kps = std::max(1, (tiles + min_splits - 1) / min_splits) * fbk::kKeyTile;
+  c->dyn_keys = n_keys;
+}
+
 fbk::AttnParams attn_common(const fb_cache* c, const void* q, int waves, int ksplit) {
   fbk::AttnParams p{};
   p.waves = waves;
@@ -204,6 +233,12 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   p.splits = choose_splits(c, n, active_groups);
   const int tiles = (n + fbk::kKeyTile - 1) / fbk::kKeyTile;
   p.keys_per_split = std::max(1, (tiles + p.splits - 1) / p.splits) * fbk::kKeyTile;
+  if (sel.flags != nullptr && dyn_possible(c) && n > 0) {
+    plan_dyn(c, n);   // heads chosen on the device: the split count follows how many groups it selects
+    p.dyn = c->dyn;
+    p.grid = c->dyn_grid;
+    p.keys_per_split = c->dyn_kps;   // the longest range the plan may pick (LDS sizing)
+  }
   p.sel = sel;
   p.part_o = c->part_o;
   p.part_l = c->part_l;
@@ -223,6 +258,8 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   cp.splits = p.splits;
   cp.batch = c->cfg.batch;
   cp.hq = c->cfg.n_q_heads;
+  cp.hkv = c->cfg.n_kv_heads;
+  cp.dyn = p.dyn;
   cp.bs = c->cfg.block_size;
   cp.row_chunks = c->row_chunks;
   cp.sel = sel;
@@ -344,7 +381,13 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
       c->n_cu = prop.multiProcessorCount;
   }
   c->splits_cap = fbk::kMaxSplits;
-  c->splits_cap = choose_splits(c, cfg->max_prefix, cfg->batch * cfg->n_kv_heads);
+  {
+    int cap = choose_splits(c, cfg->max_prefix, cfg->batch * cfg->n_kv_heads);
+    if (dyn_possible(c))   // room for the device plan's shorter ranges when few groups are active
+      for (int n = 1; n < cfg->batch * cfg->n_kv_heads; ++n)
+        cap = std::max(cap, std::min(kDynSplitCap, choose_splits(c, cfg->max_prefix, n)));
+    c->splits_cap = cap;
+  }
   if (cfg->kv_splits > 0) c->splits_cap = std::max(c->splits_cap, std::min(cfg->kv_splits, fbk::kMaxSplits));
 
   const int64_t nh = (int64_t)cfg->batch * cfg->n_q_heads;

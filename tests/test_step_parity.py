@@ -126,3 +126,39 @@ def test_deterministic():
     runs = [H.run_gpu(inp, record_cache=False)[0].out for _ in range(3)]
     for r in runs[1:]:
         assert np.array_equal(r, runs[0])
+
+
+def test_gamma_gqa_device_plan():
+    """GAMMA on GQA shapes (32 query / 8 kv heads, unscaled values): per-head
+    decisions made on the device, whose external launch then plans its splits
+    for the groups it selected.  The threshold is set from the oracle alone,
+    between two of its similarities, so that every decision has a margin."""
+    import dataclasses
+    w = wl.workload("dllm-8k").with_(value_std=1.0, steps=6, policy="gamma", gamma=2.0)
+    chosen = None
+    for prefix in (1500, 1200, 900):     # fixed search order: the first passing case is used
+        inp = wl.generate(w, prefix=prefix)
+        probe = H.run_oracle(inp)        # gamma 2: every head recomputes, every sim defined
+        sims = np.sort(probe[0].sim[1].ravel())
+        gaps = sorted(((sims[i + 1] - sims[i], i) for i in range(len(sims) // 4, 3 * len(sims) // 4)),
+                      reverse=True)
+        for _, i in gaps:
+            g = float(0.5 * (sims[i] + sims[i + 1]))
+            trial = dataclasses.replace(inp, workload=w.with_(gamma=g))
+            ref = H.run_oracle(trial)
+            defined = ref[0].sim[~np.isnan(ref[0].sim)]
+            if np.min(np.abs(defined - g)) > 1e-3:
+                chosen = (g, trial, ref)
+                break
+        if chosen is not None:
+            break
+    assert chosen is not None, "no threshold with margins above 1e-3"
+    g, trial, ref = chosen
+    print(f"[parity] gamma GQA prefix {trial.k_prefix.shape[2]} threshold {g:.6f}", flush=True)
+    gpu = H.run_gpu(trial)
+    errs = H.compare_block(gpu[0], ref[0], w.dtype, what="gamma gqa")
+    fin = ~np.isnan(ref[0].sim)
+    assert np.max(np.abs(gpu[0].sim[fin] - ref[0].sim[fin])) <= 5e-4
+    reuse = ref[0].reuse
+    assert 0 < int(reuse.sum()) < reuse[2:].size   # a mix of reused and recomputed heads
+    print(f"[parity] gamma gqa errs {errs} reused head-steps {int(reuse.sum())}", flush=True)
