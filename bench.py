@@ -259,6 +259,98 @@ def cpu_baseline(name, budget_s: float):
             "us_per_layer_step": round(1e6 * block_s / len(blk.steps), 1)}
 
 
+SWEEP_PREFIXES = (100_000, 200_000, 400_000, 800_000)
+
+
+def sweep(prefixes=SWEEP_PREFIXES, n_blocks=3):
+    """Multi-block long-context sweep on the dLLM layer shape (batch 1, 32/8
+    heads, D=128, block 32, bf16): from each starting prefix, n_blocks
+    consecutive blocks of 8 steps, the block's final K/V appended to the
+    prefix at block end (a device copy on the stream) and the cache reset;
+    the workload's threshold policy and always-recompute run on the same
+    inputs.  The prefix K/V are seeded device draws of the workload's
+    distribution (one layer; at 100k tokens its K/V are already 1.6x the
+    MALL)."""
+    import torch
+    from cached_attention_fb_amd import fb
+    from cached_attention_fb_amd import workload as wl
+
+    w = wl.workload("dllm-8k").with_(blocks=n_blocks)
+    inp = wl.generate(w, prefix=0)
+    B, Hkv, D, Bs = w.batch, w.n_kv_heads, w.head_dim, w.block
+    max_prefix = max(prefixes) + n_blocks * Bs
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    kp = torch.empty((B, Hkv, max_prefix, D), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    for t in (kp, vp):
+        for c0 in range(0, max_prefix, 65536):
+            c1 = min(max_prefix, c0 + 65536)
+            t[:, :, c0:c1].copy_(torch.randn((B, Hkv, c1 - c0, D), generator=gen, device="cuda") * w.value_std)
+    cache = fb.Cache(B, w.n_q_heads, Hkv, D, Bs, max_prefix, torch.bfloat16)
+    dev_steps = [[(st.q.cuda(), st.k.cuda(), st.v.cuda(), np.asarray(st.n_updated, dtype=np.int32)) for st in blk.steps]
+                 for blk in inp.blocks]
+    out = torch.empty_like(dev_steps[0][0][0])
+    stream = torch.cuda.current_stream().cuda_stream
+    pols = {"tau": fb.POLICY_TAU, "always": fb.POLICY_ALWAYS}
+
+    def run(P, pol, evs=None):
+        n = P
+        i = 0
+        for blk in dev_steps:
+            cache.reset(stream)
+            for (q, k, v, m) in blk:
+                cache.step(pols[pol], q, k, v, kp, vp, n, out, tau=w.tau, n_updated=m, stream=stream)
+                if evs is not None:
+                    evs[i].record()
+                i += 1
+            last_k, last_v = blk[-1][1], blk[-1][2]   # block end: its final K/V join the prefix
+            kp[:, :, n:n + Bs].copy_(last_k)
+            vp[:, :, n:n + Bs].copy_(last_v)
+            n += Bs
+
+    rows = []
+    n_steps = n_blocks * w.steps
+    for P in prefixes:
+        rec = {"prefix": P}
+        for pol in ("tau", "always"):
+            run(P, pol)   # warm-up (also writes the same appended rows)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
+            e0.record()
+            run(P, pol, evs)
+            torch.cuda.synchronize()
+            times = [1e3 * e0.elapsed_time(evs[0])] + [1e3 * evs[i - 1].elapsed_time(evs[i]) for i in range(1, n_steps)]
+            rec[f"{pol}_block_us"] = round(sum(times) / n_blocks, 2)
+            if pol == "tau":   # the host's decision: a step after the first reuses when M < tau
+                ms = [int(st[3][0]) for blk in dev_steps for st in blk]
+                full = [t for i, t in enumerate(times) if i % w.steps == 0 or ms[i] >= w.tau]
+                reuse = [t for i, t in enumerate(times) if not (i % w.steps == 0 or ms[i] >= w.tau)]
+                rec["tau_full_step_us"] = round(float(np.median(full)), 2)
+                rec["tau_reuse_step_us"] = round(float(np.median(reuse)), 2) if reuse else None
+            else:
+                rec["always_step_us"] = round(float(np.median(times)), 2)
+        rec["reuse_vs_full"] = round(rec["always_block_us"] / rec["tau_block_us"], 3)
+        # external attention alone at this prefix (events around each launch)
+        cache.profile_enable(True)
+        run(P, "always")
+        torch.cuda.synchronize()
+        prof = cache.profile_read()
+        cache.profile_enable(False)
+        ext_us = 1e3 * prof["external"][1] / max(1, prof["external"][0])
+        _, alg_bytes, _ = algorithmic(w, P + Bs)
+        rec["external_us"] = round(ext_us, 2)
+        rec["external_frac_hbm"] = round(alg_bytes / (ext_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        rows.append(rec)
+        print(json.dumps({"sweep_row": rec}), flush=True)
+    cache.close()
+    return {"metric": "multi-block long-context sweep: step time vs prefix length, threshold policy vs always-recompute",
+            "unit": "us", "higher_is_better": False, "data": "synthetic (seeded device draws; dLLM layer shape)",
+            "config": {"workload": "dllm-8k layer shape, batch 1, 32/8 heads, D=128, block 32, bf16",
+                       "blocks_per_prefix": n_blocks, "steps_per_block": w.steps, "tau": w.tau},
+            "rows": rows}
+
+
 def calibrate():
     """A plain elementwise kernel of known traffic (reads 256 MiB, writes
     256 MiB), run under the same counters as the attention kernels to scale
@@ -285,6 +377,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate", action="store_true", help="only run the known-traffic reference kernel")
+    ap.add_argument("--sweep", action="store_true", help="only run the multi-block long-context prefix sweep")
     args = ap.parse_args()
     if args.calibrate:
         calibrate()
@@ -297,6 +390,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
+    if args.sweep:
+        print(json.dumps(sweep()), flush=True)
+        return
 
     # the largest prefix one layer's K/V can take in the free device memory
     from cached_attention_fb_amd import workload as wl

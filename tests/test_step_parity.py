@@ -162,3 +162,10 @@ def test_gamma_gqa_device_plan():
     reuse = ref[0].reuse
     assert 0 < int(reuse.sum()) < reuse[2:].size   # a mix of reused and recomputed heads
     print(f"[parity] gamma gqa errs {errs} reused head-steps {int(reuse.sum())}", flush=True)
+
+
+def test_dllm_three_blocks():
+    """Block commit at the dLLM shapes in bf16: three blocks, each appending
+    its final K/V to the prefix (and resetting the cache) before the next."""
+    gpu, ref = _full_check(wl.workload("dllm-8k").with_(blocks=3, steps=4), prefix=700)
+    assert len(gpu) == 3
