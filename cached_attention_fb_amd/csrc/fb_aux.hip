@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
 }
 
 // Gamma decisions, one workgroup per head: similarity of a recomputed head
-// from the combine's partial terms (summed in a fixed order), slot flip, and
+// (or of its kv group: the same terms summed over the group's heads) from the
+// combine's partial terms (summed in a fixed order), slot flip, and
 // the reuse decision of the next step (strict sim > gamma; NaN, i.e. no
 // similarity yet, never reuses).
 __global__ __launch_bounds__(kThreads) void decide_kernel(const DecideParams p) {
@@ -124,8 +125,12 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(const DecideParams p) 
   __syncthreads();   // every thread has read the flags before thread 0 updates them
   if (computed && had_value) {   // workgroup-uniform
     float dot = 0.0f, nn = 0.0f, no = 0.0f;
-    for (int c = tid; c < p.row_chunks; c += kThreads) {
-      const float* t = p.cos_part + ((int64_t)bh * p.row_chunks + c) * 3;
+    // the terms of the head, or of every head of its group (in head order,
+    // so that the heads of a group obtain the same sum)
+    const int h0 = bh - (bh % p.hq) % p.group;
+    const int terms = p.group * p.row_chunks;
+    for (int c = tid; c < terms; c += kThreads) {
+      const float* t = p.cos_part + ((int64_t)h0 * p.row_chunks + c) * 3;
       dot += t[0];
       nn += t[1];
       no += t[2];

@@ -90,6 +90,7 @@ struct CombineParams {
 struct DecideParams {
   int32_t n_heads;        // B*Hq
   int32_t hq, row_chunks;
+  int32_t group;          // 1: a similarity per head; G = Hq/Hkv: one per kv group (its heads' terms summed)
   const uint8_t* reuse_now;  // decisions applied at this step
   uint8_t* reuse_next;       // decisions for the next step
   uint8_t* cur;

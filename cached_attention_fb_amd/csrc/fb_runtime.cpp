@@ -94,6 +94,7 @@ struct fb_cache {
   int32_t block_prefix = -1; // prefix_len of the current block
   int32_t block_policy = -1;
   std::vector<uint8_t> host_valid;   // [B]: every head of b holds a computed A_out (tau bookkeeping)
+  std::vector<int64_t> cum_updated;  // [B]: TAU_CUM, updated tokens summed since b's last computation
   // profiling
   bool prof = false;
   std::vector<ProfRec> prof_recs;
@@ -320,6 +321,7 @@ fb_status run_reset(fb_cache* c, hipStream_t s) {
   c->block_prefix = -1;
   c->block_policy = -1;
   std::fill(c->host_valid.begin(), c->host_valid.end(), 0);
+  std::fill(c->cum_updated.begin(), c->cum_updated.end(), 0);
   return FB_OK;
 }
 
@@ -375,6 +377,7 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
   c->row_chunks = (cfg->block_size + crows - 1) / crows;
   c->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
   c->host_valid.assign(cfg->batch, 0);
+  c->cum_updated.assign(cfg->batch, 0);
   {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
@@ -482,8 +485,11 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   if (!c) return fail(FB_E_ARG, "cache is null");
   if (!pa) return fail(FB_E_ARG, "policy args are null");
   if (!q_blk || !k_blk || !v_blk || !out) return fail(FB_E_ARG, "a tensor pointer is null");
-  if (pa->policy != FB_POLICY_ALWAYS && pa->policy != FB_POLICY_TAU && pa->policy != FB_POLICY_GAMMA)
+  if (pa->policy != FB_POLICY_ALWAYS && pa->policy != FB_POLICY_TAU && pa->policy != FB_POLICY_GAMMA &&
+      pa->policy != FB_POLICY_TAU_CUM && pa->policy != FB_POLICY_GAMMA_GROUP)
     return fail(FB_E_ARG, "unknown policy %d", pa->policy);
+  const bool tau_like = pa->policy == FB_POLICY_TAU || pa->policy == FB_POLICY_TAU_CUM;
+  const bool gamma_like = pa->policy == FB_POLICY_GAMMA || pa->policy == FB_POLICY_GAMMA_GROUP;
   if (prefix_len < 0 || prefix_len > c->cfg.max_prefix)
     return fail(FB_E_SHAPE, "prefix_len %d outside [0, max_prefix=%d]", prefix_len, c->cfg.max_prefix);
   if (prefix_len > 0 && (!k_prefix || !v_prefix)) return fail(FB_E_ARG, "k_prefix/v_prefix is null");
@@ -496,20 +502,24 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   // sequences whose heads recompute the external part (TAU decides per sequence)
   fbk::HeadSel sel{};
   int active = 0;
-  if (pa->policy == FB_POLICY_TAU) {
+  if (tau_like) {
     if (pa->tau < 0) return fail(FB_E_ARG, "tau %d is negative", pa->tau);
     if (!pa->n_updated) return fail(FB_E_ARG, "n_updated is null under the tau policy");
     for (int b = 0; b < B; ++b)
       if (pa->n_updated[b] < 0) return fail(FB_E_ARG, "n_updated[%d] = %d is negative", b, pa->n_updated[b]);
   }
+  if (gamma_like && !(pa->gamma == pa->gamma)) return fail(FB_E_ARG, "gamma is NaN");
+  std::vector<uint8_t> reuse_seq(B, 0);
   for (int b = 0; b < B; ++b) {
-    const bool reuse = pa->policy == FB_POLICY_TAU && c->host_valid[b] && pa->n_updated[b] < pa->tau;
+    bool reuse = false;
+    if (pa->policy == FB_POLICY_TAU) reuse = c->host_valid[b] && pa->n_updated[b] < pa->tau;
+    if (pa->policy == FB_POLICY_TAU_CUM) reuse = c->host_valid[b] && c->cum_updated[b] + pa->n_updated[b] < pa->tau;
+    reuse_seq[b] = reuse ? 1 : 0;
     if (!reuse) {
       sel.seq_bits[b >> 5] |= 1u << (b & 31);
       ++active;
     }
   }
-  if (pa->policy == FB_POLICY_GAMMA && !(pa->gamma == pa->gamma)) return fail(FB_E_ARG, "gamma is NaN");
   DeviceGuard g(c->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "set device");
   hipStream_t s = (hipStream_t)stream;
@@ -518,7 +528,7 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   uint8_t* reuse_next = c->reuse + ((c->steps + 1) & 1) * nh;
 
   fb_status st = FB_OK;
-  if (pa->policy == FB_POLICY_GAMMA) {
+  if (gamma_like) {
     sel = all_heads(c);
     sel.flags = reuse_now;
     sel.flags_select = 0;   // compute the heads not marked for reuse
@@ -535,6 +545,7 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
     dp.sim = c->sim;
     dp.cos_part = c->cos_part;
     dp.gamma = pa->gamma;
+    dp.group = pa->policy == FB_POLICY_GAMMA_GROUP ? c->group : 1;
     ProfRec r;
     prof_begin(c, s, &r, 3);
     hipError_t e = fbk::launch_decide(dp, s);
@@ -549,7 +560,11 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
       if (st != FB_OK) return st;
     }
     st = run_internal(c, q_blk, k_blk, v_blk, out, sel, reuse_now, s);
-    std::fill(c->host_valid.begin(), c->host_valid.end(), 1);
+    if (st == FB_OK) {
+      std::fill(c->host_valid.begin(), c->host_valid.end(), 1);
+      for (int b = 0; b < B; ++b)   // TAU_CUM: the sum restarts where a sequence recomputed
+        c->cum_updated[b] = reuse_seq[b] ? c->cum_updated[b] + pa->n_updated[b] : 0;
+    }
   }
   if (st != FB_OK) return st;
   if (c->steps == 0) {

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfb.so")
 
 FB_OK, FB_E_ARG, FB_E_SHAPE, FB_E_DTYPE, FB_E_STATE, FB_E_NOMEM, FB_E_HIP, FB_E_UNSUPPORTED = range(8)
 FB_F32, FB_BF16 = 0, 1
-POLICY_ALWAYS, POLICY_TAU, POLICY_GAMMA = 0, 1, 2
+POLICY_ALWAYS, POLICY_TAU, POLICY_GAMMA, POLICY_TAU_CUM, POLICY_GAMMA_GROUP = 0, 1, 2, 3, 4
 FIELD_A_OUT, FIELD_L_OUT, FIELD_SIM, FIELD_REUSE, FIELD_VALID = range(5)
 PROFILE_KINDS = 8
 KIND_NAMES = ["external", "combine", "internal_merge", "decide", "reset"]

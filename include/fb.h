@@ -63,7 +63,15 @@ enum {
 };
 
 enum { FB_F32 = 0, FB_BF16 = 1 };
-enum { FB_POLICY_ALWAYS = 0, FB_POLICY_TAU = 1, FB_POLICY_GAMMA = 2 };
+/* ALWAYS: recompute every step.  TAU (page §2, threshold reuse) and GAMMA
+ * (page §2, per-head selection): see fb_policy_args.  Two variants at the
+ * edges of those rules: TAU_CUM counts the updated tokens summed since the
+ * sequence's cache was computed, this step's included; GAMMA_GROUP decides
+ * per (sequence, kv head) with one similarity over the group's query heads
+ * (their A_out taken as one vector), so a decision matches the K/V stream it
+ * saves. */
+enum { FB_POLICY_ALWAYS = 0, FB_POLICY_TAU = 1, FB_POLICY_GAMMA = 2, FB_POLICY_TAU_CUM = 3,
+       FB_POLICY_GAMMA_GROUP = 4 };
 enum {
   FB_FIELD_A_OUT = 0,    /* float [B][Hq][Bs][D]  current cached A_out of every head */
   FB_FIELD_L_OUT = 1,    /* float [B][Hq][Bs]     current cached L_out */
@@ -129,11 +137,14 @@ fb_status fb_internal_attn_merge(fb_cache* c, const void* q_blk, const void* k_b
 typedef struct {
   int32_t policy;            /* FB_POLICY_* */
   int32_t tau;               /* TAU: reuse iff the cache holds a computed A_out and
-                                n_updated[b] < tau (strict) */
+                                n_updated[b] < tau (strict); TAU_CUM: iff the sum of
+                                n_updated[b] since the last computation, this step's
+                                included, is < tau */
   float gamma;               /* GAMMA: reuse iff the head holds a similarity and it
-                                is > gamma (strict) */
+                                is > gamma (strict); GAMMA_GROUP: the same with the
+                                group's similarity */
   const int32_t* n_updated;  /* host int32 [B]: tokens of the block updated since the
-                                previous step (TAU only; ignored otherwise) */
+                                previous step (TAU, TAU_CUM; ignored otherwise) */
 } fb_policy_args;
 
 /* One denoising step (page §2): decide per head whether to reuse the cached

@@ -52,6 +52,11 @@ import numpy as np
 ALWAYS = "always"
 TAU = "tau"
 GAMMA = "gamma"
+# Variants at the edges of the two rules (the same passages; not the pages'
+# own choices): M summed since the head's last computation, and one similarity
+# per group of query heads that share a key/value head.
+TAU_CUM = "tau_cum"
+GAMMA_GROUP = "gamma_group"
 
 
 def default_scale(head_dim: int) -> float:
@@ -130,6 +135,7 @@ class HeadState:
     sim: Optional[float] = None
     a_out: Optional[np.ndarray] = None
     l_out: Optional[np.ndarray] = None
+    cum: int = 0   # tau_cum: updated tokens summed since the last computation
 
 
 def decide(policy: str, st: HeadState, n_updated: int, tau: int, gamma: float) -> bool:
@@ -139,13 +145,20 @@ def decide(policy: str, st: HeadState, n_updated: int, tau: int, gamma: float) -
     * tau (§2 "Réutilisation basée sur un seuil"): reuse when the cache holds
       something and the number of updated tokens M is strictly below tau;
     * gamma (§2 "Sélection par tête"): reuse when the cache holds something and
-      the head's last measured similarity strictly exceeds gamma.
+      the head's last measured similarity strictly exceeds gamma;
+    * tau_cum (variant of tau): the updated tokens are summed over the steps
+      since the cache was computed, this step's included, and compared
+      strictly with tau;
+    * gamma_group (variant of gamma): the similarity is that of the head's
+      group (see run_block).
     """
     if policy == ALWAYS or not st.valid:
         return False
     if policy == TAU:
         return n_updated < tau
-    if policy == GAMMA:
+    if policy == TAU_CUM:
+        return st.cum + n_updated < tau
+    if policy in (GAMMA, GAMMA_GROUP):
         return st.sim is not None and st.sim > gamma
     raise ValueError(f"unknown policy {policy!r}")
 
@@ -179,7 +192,10 @@ def run_block(k_prefix: np.ndarray, v_prefix: np.ndarray, n_prefix: int,
     cache; always compute A_in/L_in over the block J_in; output = merge of the
     cached external part with the fresh internal part (§2 "Mécanisme
     Central").  Query head h reads key/value head h // (Hq/Hkv).  Heads are
-    independent of one another, so any subset can be evaluated alone."""
+    independent of one another, so any subset can be evaluated alone; under
+    gamma_group the heads of a group decide together (one similarity, the
+    cosine of the group's A_out tensors taken as one vector), so the group of
+    every requested head is evaluated."""
     s0 = steps[0]
     n_steps = len(steps)
     bsz, hq, bs, d = s0.q.shape
@@ -192,25 +208,36 @@ def run_block(k_prefix: np.ndarray, v_prefix: np.ndarray, n_prefix: int,
     l_rec = np.full((n_steps, bsz, hq, bs), np.nan)
     reuse = np.full((n_steps, bsz, hq), -1, dtype=np.int8)
     sim = np.full((n_steps, bsz, hq), np.nan)
-    for b, h in heads:
-        g = h // group
+    if policy == GAMMA_GROUP:
+        units = [[(b, g * group + i) for i in range(group)] for b, g in sorted({(b, h // group) for b, h in heads})]
+    else:
+        units = [[bh] for bh in heads]
+    for unit in units:
+        b, g = unit[0][0], unit[0][1] // group
         kp = k_prefix[b, g, :n_prefix]
         vp = v_prefix[b, g, :n_prefix]
-        st = HeadState()
+        sts = [HeadState() for _ in unit]   # heads of a unit decide together (one head unless gamma_group)
         for s, step in enumerate(steps):
-            q = step.q[b, h]
-            r = decide(policy, st, int(step.n_updated[b]), tau, gamma)
+            m = int(step.n_updated[b])
+            r = decide(policy, sts[0], m, tau, gamma)
             if not r:
-                a_new, l_new = attend(q, kp, vp, scale)
-                if policy == GAMMA and st.valid:
-                    st.sim = cosine(a_new, st.a_out)
-                st.a_out, st.l_out, st.valid = a_new, l_new, True
-            a_in, l_in = attend(q, step.k[b, g], step.v[b, g], scale)
-            out[s, b, h], _ = merge(st.a_out, st.l_out, a_in, l_in)
-            a_rec[s, b, h] = st.a_out
-            l_rec[s, b, h] = st.l_out
-            reuse[s, b, h] = 1 if r else 0
-            sim[s, b, h] = np.nan if st.sim is None else st.sim
+                news = [attend(step.q[b, h], kp, vp, scale) for _, h in unit]
+                if policy in (GAMMA, GAMMA_GROUP) and sts[0].valid:
+                    sim_u = cosine(np.stack([a for a, _ in news]), np.stack([st.a_out for st in sts]))
+                    for st in sts:
+                        st.sim = sim_u
+                for st, (a_new, l_new) in zip(sts, news):
+                    st.a_out, st.l_out, st.valid, st.cum = a_new, l_new, True, 0
+            else:
+                for st in sts:
+                    st.cum += m
+            for st, (_, h) in zip(sts, unit):
+                a_in, l_in = attend(step.q[b, h], step.k[b, g], step.v[b, g], scale)
+                out[s, b, h], _ = merge(st.a_out, st.l_out, a_in, l_in)
+                a_rec[s, b, h] = st.a_out
+                l_rec[s, b, h] = st.l_out
+                reuse[s, b, h] = 1 if r else 0
+                sim[s, b, h] = np.nan if st.sim is None else st.sim
     return BlockResult(out, a_rec, l_rec, reuse, sim)
 
 

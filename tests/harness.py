@@ -13,7 +13,8 @@ import oracle
 from cached_attention_fb_amd import fb
 from cached_attention_fb_amd import workload as wl
 
-POLICY_CODE = {"always": fb.POLICY_ALWAYS, "tau": fb.POLICY_TAU, "gamma": fb.POLICY_GAMMA}
+POLICY_CODE = {"always": fb.POLICY_ALWAYS, "tau": fb.POLICY_TAU, "gamma": fb.POLICY_GAMMA,
+               "tau_cum": fb.POLICY_TAU_CUM, "gamma_group": fb.POLICY_GAMMA_GROUP}
 
 
 @dataclass

@@ -330,9 +330,75 @@ def pin_multi_block_append():
         assert np.max(np.abs(r2.out[0, 0, h] - _exact(kp2, vp2, n + bs, blk2[0], 0, h, hq))) <= TOL
 
 
+def pin_tau_cum_policy():
+    """Cumulative variant: the updated tokens are summed since the cache was
+    computed; a worked sequence, and its special cases."""
+    rng = _rng(13)
+    b, hq, hkv, bs, d, n = 1, 2, 1, 8, 8, 20
+    kp, vp = rng.standard_normal((b, hkv, n, d)), rng.standard_normal((b, hkv, n, d))
+    m_list = [[0], [3], [3], [3], [0], [5], [1]]
+    steps = _steps(rng, b, hq, hkv, bs, d, m_list)
+    res = fb.run_block(kp, vp, n, steps, fb.TAU_CUM, tau=5)
+    # sums since the last computation: 3 (reuse), 6 (compute), 3, 3, 8 (compute), 1
+    assert [int(res.reuse[s, 0, 0]) for s in range(len(m_list))] == [0, 1, 0, 1, 1, 0, 1]
+    for s in (0, 2, 5):   # computed steps are exact attention
+        for h in range(hq):
+            assert np.max(np.abs(res.out[s, 0, h] - _exact(kp, vp, n, steps[s], 0, h, hq))) <= TOL
+    assert np.array_equal(res.a_out[4], res.a_out[2]) and np.array_equal(res.a_out[6], res.a_out[5])
+    # the per-step rule on the same inputs reuses at every step with M < 5
+    res_tau = fb.run_block(kp, vp, n, steps, fb.TAU, tau=5)
+    assert [int(res_tau.reuse[s, 0, 0]) for s in range(len(m_list))] == [0, 1, 1, 1, 1, 0, 1]
+    # tau = 0 never reuses; M = 0 throughout reuses from step 1 and stays exact
+    assert np.all(fb.run_block(kp, vp, n, steps, fb.TAU_CUM, tau=0).reuse == 0)
+    steps0 = _steps(rng, b, hq, hkv, bs, d, [[0]] * 4)
+    r0 = fb.run_block(kp, vp, n, steps0, fb.TAU_CUM, tau=1)
+    assert np.all(r0.reuse[1:] == 1)
+    for s, st in enumerate(steps0):
+        for h in range(hq):
+            assert np.max(np.abs(r0.out[s, 0, h] - _exact(kp, vp, n, st, 0, h, hq))) <= TOL
+
+
+def pin_gamma_group_policy():
+    """Group variant: one similarity per group of query heads sharing a kv
+    head, the cosine of their A_out taken as one vector."""
+    rng = _rng(14)
+    hq, hkv, bs, d, n = 4, 2, 6, 8, 30
+    kp, vp = rng.standard_normal((1, hkv, n, d)), rng.standard_normal((1, hkv, n, d))
+    sigma = np.array([0.02, 0.6, 0.05, 0.04])
+    qb = rng.standard_normal((1, hq, bs, d))
+    k = rng.standard_normal((1, hkv, bs, d))
+    v = rng.standard_normal((1, hkv, bs, d))
+    steps = [fb.StepData(qb + sigma[None, :, None, None] * rng.standard_normal(qb.shape), k, v,
+                         np.full(1, bs, dtype=np.int32)) for _ in range(5)]
+    res = fb.run_block(kp, vp, n, steps, fb.GAMMA_GROUP, gamma=2.0)   # never reuses: every sim defined
+    sc = fb.default_scale(d)
+    for s in range(1, 5):
+        for g in range(hkv):
+            new = np.concatenate([fb.attend(steps[s].q[0, h], kp[0, g], vp[0, g], sc)[0].ravel()
+                                  for h in (2 * g, 2 * g + 1)])
+            old = np.concatenate([fb.attend(steps[s - 1].q[0, h], kp[0, g], vp[0, g], sc)[0].ravel()
+                                  for h in (2 * g, 2 * g + 1)])
+            ref = 1.0 - scipy.spatial.distance.cosine(new, old)
+            assert abs(res.sim[s, 0, 2 * g] - ref) <= 1e-12 and res.sim[s, 0, 2 * g + 1] == res.sim[s, 0, 2 * g]
+    # the decision is shared by the group: the loud head 1 keeps group 0 recomputing
+    resg = fb.run_block(kp, vp, n, steps, fb.GAMMA_GROUP, gamma=0.97)
+    assert np.all(resg.reuse[:, 0, 0] == resg.reuse[:, 0, 1]) and np.all(resg.reuse[:, 0, 2] == resg.reuse[:, 0, 3])
+    assert np.all(resg.reuse[:, 0, 0] == 0) and np.all(resg.reuse[2:, 0, 2] == 1)
+    resh = fb.run_block(kp, vp, n, steps, fb.GAMMA, gamma=0.97)
+    assert np.all(resh.reuse[2:, 0, 0] == 1)      # per head, the quiet head 0 would reuse
+    # groups of one head: identical to the per-head rule
+    kp1, vp1 = rng.standard_normal((1, hq, n, d)), rng.standard_normal((1, hq, n, d))
+    steps1 = _video_steps(rng, hq, bs, d, np.array([0.02, 0.3, 0.05, 1.0]), 5)
+    a = fb.run_block(kp1, vp1, n, steps1, fb.GAMMA_GROUP, gamma=0.95)
+    bres = fb.run_block(kp1, vp1, n, steps1, fb.GAMMA, gamma=0.95)
+    assert np.array_equal(a.reuse, bres.reuse) and np.array_equal(a.out, bres.out)
+    assert np.array_equal(np.nan_to_num(a.sim, nan=-9), np.nan_to_num(bres.sim, nan=-9))
+
+
 PINS = [pin_attend_bruteforce, pin_attend_vs_torch, pin_external_gqa_vs_torch, pin_attend_closed_forms,
         pin_attend_permutation_invariance, pin_merge_equals_full_attention, pin_merge_special_cases,
-        pin_split_associativity, pin_cosine, pin_tau_policy, pin_gamma_policy, pin_multi_block_append]
+        pin_split_associativity, pin_cosine, pin_tau_policy, pin_gamma_policy, pin_multi_block_append,
+        pin_tau_cum_policy, pin_gamma_group_policy]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -405,6 +471,24 @@ def _decide_ignore_valid(policy, st, n_updated, tau, gamma):
     return _real_decide(policy, st, n_updated, tau, gamma)
 
 
+def _decide_cum_le(policy, st, n_updated, tau, gamma):
+    if policy == fb.TAU_CUM and st.valid:
+        return st.cum + n_updated <= tau
+    return _real_decide(policy, st, n_updated, tau, gamma)
+
+
+def _decide_cum_per_step(policy, st, n_updated, tau, gamma):
+    if policy == fb.TAU_CUM and st.valid:
+        return n_updated < tau   # forgets the sum since the last computation
+    return _real_decide(policy, st, n_updated, tau, gamma)
+
+
+def _cosine_mean_of_rows(a, o):
+    # averages the similarity of the stacked parts instead of one cosine over all of them
+    a, o = np.atleast_2d(np.asarray(a, dtype=np.float64).reshape(len(a), -1)), np.atleast_2d(np.asarray(o).reshape(len(o), -1))
+    return float(np.mean([_real_cosine(x, y) for x, y in zip(a, o)]))
+
+
 def _cosine_unclamped_l1(a, o):
     a, o = np.ravel(a), np.ravel(o)
     na, no = np.abs(a).sum(), np.abs(o).sum()
@@ -431,7 +515,8 @@ MUTANTS = [
     ("attend", _attend_kv_swapped), ("attend", _attend_unnormalised),
     ("merge", _merge_sign), ("merge", _merge_no_denominator), ("merge", _merge_drop_in),
     ("decide", _decide_le), ("decide", _decide_ge), ("decide", _decide_ignore_valid),
-    ("cosine", _cosine_unclamped_l1), ("cosine", _cosine_no_abs),
+    ("cosine", _cosine_unclamped_l1), ("cosine", _cosine_no_abs), ("cosine", _cosine_mean_of_rows),
+    ("decide", _decide_cum_le), ("decide", _decide_cum_per_step),
     ("external", _external_mod_group),
 ]
 

@@ -169,3 +169,41 @@ def test_dllm_three_blocks():
     its final K/V to the prefix (and resetting the cache) before the next."""
     gpu, ref = _full_check(wl.workload("dllm-8k").with_(blocks=3, steps=4), prefix=700)
     assert len(gpu) == 3
+
+
+def test_tau_cumulative_variant():
+    """Cumulative threshold variant on the dLLM shapes: decisions bit-exact."""
+    gpu, ref = _full_check(wl.workload("dllm-8k").with_(steps=8), prefix=1000, policy="tau_cum")
+    per_step = H.run_oracle(wl.generate(wl.workload("dllm-8k").with_(steps=8), prefix=1000), policy="tau")
+    assert int(ref[0].reuse.sum()) < int(per_step[0].reuse.sum())   # the sum recomputes sooner
+
+
+def test_gamma_group_variant_gqa():
+    """Group-granular similarity on GQA shapes: one decision per kv group, from
+    the cosine over the group's heads; threshold from the oracle alone."""
+    import dataclasses
+    w = wl.workload("dllm-8k").with_(value_std=1.0, steps=6, policy="gamma_group", gamma=2.0)
+    chosen = None
+    for prefix in (1500, 1200, 900):
+        inp = wl.generate(w, prefix=prefix)
+        probe = H.run_oracle(inp)
+        sims = np.sort(np.unique(probe[0].sim[1].ravel()))   # one value per group
+        for i in range(len(sims) - 1):
+            g = float(0.5 * (sims[i] + sims[i + 1]))
+            trial = dataclasses.replace(inp, workload=w.with_(gamma=g))
+            ref = H.run_oracle(trial)
+            defined = ref[0].sim[~np.isnan(ref[0].sim)]
+            if np.min(np.abs(defined - g)) > 1e-3 and 0 < int(ref[0].reuse.sum()) < ref[0].reuse[2:].size:
+                chosen = (g, trial, ref)
+                break
+        if chosen is not None:
+            break
+    assert chosen is not None, "no threshold with margins above 1e-3"
+    g, trial, ref = chosen
+    print(f"[parity] gamma_group prefix {trial.k_prefix.shape[2]} threshold {g:.6f}", flush=True)
+    gpu = H.run_gpu(trial)
+    H.compare_block(gpu[0], ref[0], w.dtype, what="gamma_group")
+    fin = ~np.isnan(ref[0].sim)
+    assert np.max(np.abs(gpu[0].sim[fin] - ref[0].sim[fin])) <= 5e-4
+    r = ref[0].reuse.reshape(ref[0].reuse.shape[0], w.batch, w.n_kv_heads, -1)
+    assert np.all(r == r[..., :1])   # the heads of a group decide together
