@@ -99,7 +99,8 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
     layers = layers or max(1, math.ceil(2.5 * MALL_BYTES / kv_bytes))
     dev = "cuda"
     policy_name = policy_name or w.policy
-    policy = {"tau": fb.POLICY_TAU, "gamma": fb.POLICY_GAMMA, "always": fb.POLICY_ALWAYS}[policy_name]
+    policy = {"tau": fb.POLICY_TAU, "gamma": fb.POLICY_GAMMA, "always": fb.POLICY_ALWAYS,
+              "tau_cum": fb.POLICY_TAU_CUM, "gamma_group": fb.POLICY_GAMMA_GROUP}[policy_name]
 
     # device inputs: per-layer prefix K/V and caches; step inputs shared by the layers
     kp0 = inp.k_prefix.to(dev)
@@ -210,6 +211,43 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
         "kernel_us": kernel_us, "roofline": roof, "policy": policy_name,
         "step_full_us": step_full_us, "step_reuse_us": step_reuse_us,
     }
+
+
+def staleness(name, policies):
+    """Output error of each reuse policy against always-recompute on the same
+    seeded block (one layer): max |out - out_always| / max |out_always| and the
+    RMS error over the RMS of out_always, over the block's steps, and the
+    fraction of (step, head) pairs that reused."""
+    import torch
+    from cached_attention_fb_amd import fb
+    from cached_attention_fb_amd import workload as wl
+
+    codes = {"always": fb.POLICY_ALWAYS, "tau": fb.POLICY_TAU, "gamma": fb.POLICY_GAMMA,
+             "tau_cum": fb.POLICY_TAU_CUM, "gamma_group": fb.POLICY_GAMMA_GROUP}
+    w = wl.workload(name)
+    inp = wl.generate(w)
+    blk = inp.blocks[0]
+    kp, vp = inp.k_prefix.cuda(), inp.v_prefix.cuda()
+    cache = fb.Cache(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block, w.prefix, w.torch_dtype)
+    outs = {}
+    reuse = {}
+    for pol in ("always",) + tuple(policies):
+        cache.reset()
+        o, r = [], []
+        for st in blk.steps:
+            out = torch.empty_like(st.q, device="cuda")
+            cache.step(codes[pol], st.q.cuda(), st.k.cuda(), st.v.cuda(), kp, vp, w.prefix, out,
+                       tau=w.tau, gamma=w.gamma, n_updated=st.n_updated)
+            o.append(out.float().cpu())
+            r.append(cache.read(fb.FIELD_REUSE).astype(np.int64))
+        outs[pol], reuse[pol] = torch.stack(o), np.stack(r)
+    cache.close()
+    ref = outs["always"]
+    scale = float(ref.abs().max())
+    rms = float(ref.pow(2).mean().sqrt())
+    return {pol: {"max_rel_err_vs_always": round(float((outs[pol] - ref).abs().max()) / scale, 6),
+                  "rms_rel_err_vs_always": round(float((outs[pol] - ref).pow(2).mean().sqrt()) / rms, 6),
+                  "reused_fraction": round(float(reuse[pol].mean()), 4)} for pol in policies}
 
 
 def traffic_for(name):
@@ -370,7 +408,7 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="dllm-8k")
-    ap.add_argument("--policy", default=None, choices=[None, "tau", "gamma", "always"])
+    ap.add_argument("--policy", default=None, choices=[None, "tau", "gamma", "always", "tau_cum", "gamma_group"])
     ap.add_argument("--layers", type=int, default=0, help="0: enough layers to exceed 2.5x the MALL")
     ap.add_argument("--splits", type=int, default=0, help="0: automatic split-KV count")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -447,6 +485,19 @@ def main():
                                                            "avg_launch_us")},
                            "kernel_avg_us_always": e["kernel_us"]}
         result["workloads"] = extra
+        # threshold variants (per-step vs cumulative M): step time, reuse and
+        # output error against always-recompute on the same block
+        variants = {}
+        for name, pols in (("dllm-8k", ("tau", "tau_cum")), ("long-32k-b4", ("tau", "tau_cum"))):
+            S = wl.workload(name).steps
+            err = staleness(name, pols)
+            variants[name] = {}
+            for pol in pols:
+                e = measure(name, 2 * S, S, policy_name=pol, decisions=False)
+                variants[name][pol] = {"us_per_layer_step": round(e["per_layer_step_us"], 2),
+                                       "reuse_vs_full_speedup": round(e["always_layer_step_us"] / e["per_layer_step_us"], 3),
+                                       **err[pol]}
+        result["policy_variants"] = variants
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
     print(json.dumps(result), flush=True)
