@@ -213,6 +213,94 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
     }
 
 
+def graph_bench(name, blocks=8, warmup=2):
+    """Threshold decisions made on the device (counts in device memory), run
+    eagerly and as one HIP graph per block (reset + every step of every layer,
+    recorded by stream capture), beside host decisions run eagerly: µs per
+    layer-step under the workload's threshold and under always-recompute, and
+    the host's time per fb_step call while enqueueing."""
+    import torch
+    from cached_attention_fb_amd import fb
+    from cached_attention_fb_amd import workload as wl
+
+    w = wl.workload(name)
+    inp = wl.generate(w)
+    blk = inp.blocks[0]
+    S = len(blk.steps)
+    n = w.prefix
+    kv_bytes, _, _ = algorithmic(w, n)
+    layers = max(1, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+    pol = {"tau": fb.POLICY_TAU, "tau_cum": fb.POLICY_TAU_CUM}[w.policy]
+    dev = "cuda"
+    kp0 = inp.k_prefix.to(dev)
+    vp0 = inp.v_prefix.to(dev)
+    prefixes = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(layers - 1)]
+    caches = [fb.Cache(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block, n, w.torch_dtype)
+              for _ in range(layers)]
+    qs = [st.q.to(dev) for st in blk.steps]
+    ks = [st.k.to(dev) for st in blk.steps]
+    vs = [st.v.to(dev) for st in blk.steps]
+    ms_host = [np.ascontiguousarray(st.n_updated, dtype=np.int32) for st in blk.steps]
+    ms_dev = [torch.as_tensor(m).to(dev) for m in ms_host]
+    ms_ptr = [m.data_ptr() for m in ms_dev]
+    del inp, blk
+    outs = [torch.empty_like(qs[0]) for _ in range(layers)]
+    prepared = [[c.prepare(qs[s], ks[s], vs[s], prefixes[li][0], prefixes[li][1], outs[li]) for s in range(S)]
+                for li, c in enumerate(caches)]
+
+    def block(mode, stream):
+        for s in range(S):
+            for li in range(layers):
+                if s == 0:
+                    caches[li].reset(stream)
+                if mode == "host":
+                    prepared[li][s](pol, n, ms_host[s], w.tau, 0.0, stream)
+                elif mode == "device":
+                    prepared[li][s](pol, n, None, w.tau, 0.0, stream, n_updated_dev=ms_ptr[s])
+                else:
+                    prepared[li][s](fb.POLICY_ALWAYS, n, None, 0, 0.0, stream)
+
+    cur = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        t0 = time.perf_counter()
+        for _ in range(blocks):
+            fn()
+        t1 = time.perf_counter()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / (blocks * S * layers), 1e6 * (t1 - t0) / (blocks * S * layers)
+
+    res = {"workload": name, "layers": layers, "steps_per_block": S, "blocks": blocks}
+    for mode in ("host", "device", "always"):
+        us, enq = timed(lambda: block(mode, cur.cuda_stream))
+        res[f"eager_{mode}_us_per_layer_step"] = round(us, 3)
+        res[f"eager_{mode}_enqueue_us_per_call"] = round(enq, 3)
+    side = torch.cuda.Stream()
+    for mode in ("device", "always"):
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            block(mode, side.cuda_stream)
+        torch.cuda.synchronize()
+        us, enq = timed(g.replay)
+        res[f"graph_{mode}_us_per_layer_step"] = round(us, 3)
+        del g
+    res["graph_reuse_vs_full_speedup"] = round(res["graph_always_us_per_layer_step"] /
+                                               res["graph_device_us_per_layer_step"], 3)
+    for c in caches:
+        c.close()
+    del prepared, caches, prefixes, kp0, vp0, qs, ks, vs, outs, ms_dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def staleness(name, policies):
     """Output error of each reuse policy against always-recompute on the same
     seeded block (one layer): max |out - out_always| / max |out_always| and the
@@ -416,6 +504,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate", action="store_true", help="only run the known-traffic reference kernel")
     ap.add_argument("--sweep", action="store_true", help="only run the multi-block long-context prefix sweep")
+    ap.add_argument("--graph", action="store_true",
+                    help="only run device-side threshold decisions, eager and as HIP graphs")
     args = ap.parse_args()
     if args.calibrate:
         calibrate()
@@ -430,6 +520,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         print(json.dumps(sweep()), flush=True)
+        return
+    if args.graph:
+        print(json.dumps(graph_bench(args.workload)), flush=True)
         return
 
     # the largest prefix one layer's K/V can take in the free device memory
@@ -498,6 +591,8 @@ def main():
                                        "reuse_vs_full_speedup": round(e["always_layer_step_us"] / e["per_layer_step_us"], 3),
                                        **err[pol]}
         result["policy_variants"] = variants
+        # threshold decisions on the device, eager and replayed as HIP graphs
+        result["device_decisions"] = graph_bench(w.name if w.policy in ("tau", "tau_cum") else "dllm-8k")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
     print(json.dumps(result), flush=True)

@@ -47,6 +47,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = lane & 31, hl = lane >> 5;
   const AttnItem it = attn_item(p, MODE == kModePartial);
+  if constexpr (MODE == kModePartial) record_decisions(p);
+  else update_cum(p, it.b, it.g, it.rt);
   if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
   const int b = it.b, g = it.g, grp = p.hq / p.hkv;
   const int key_begin = it.key_begin, key_end = it.key_end;

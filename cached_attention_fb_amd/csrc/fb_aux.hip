@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kThreads) void reset_kernel(const ResetParams p) {
   p.reuse[bh] = 0;
   p.reuse[p.n_heads + bh] = 0;
   p.sim[bh] = __builtin_nanf("");
+  if (p.cum != nullptr && bh < p.batch) p.cum[bh] = 0;
 }
 
 }  // namespace

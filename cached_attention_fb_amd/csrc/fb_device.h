@@ -58,8 +58,33 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 
 __device__ __forceinline__ bool head_selected(const HeadSel& s, int b, int bh) {
   if (!((s.seq_bits[b >> 5] >> (b & 31)) & 1u)) return false;
+  if (s.m != nullptr) {   // threshold rule with the updated-token counts in device memory
+    const int64_t upd = (int64_t)s.m[b] + (s.cum != nullptr ? s.cum[b] : 0);
+    return !(s.valid[bh] != 0 && upd < s.tau);
+  }
   if (s.flags == nullptr) return true;
   return (s.flags[bh] != 0) == (s.flags_select != 0);
+}
+
+// Partial launches whose heads are decided in the kernel: the first workgroup
+// records 1 - selected for every head, which the launches after it select
+// from (they may change what the decision reads).  Runs before any early exit.
+__device__ __forceinline__ void record_decisions(const AttnParams& p) {
+  if (p.reuse_rec == nullptr || blockIdx.x != 0) return;
+  const int nh = p.batch * p.hq;
+  for (int bh = threadIdx.x; bh < nh; bh += blockDim.x)
+    p.reuse_rec[bh] = head_selected(p.sel, bh / p.hq, bh) ? 0 : 1;
+}
+
+// Merge launches under the cumulative threshold decided on the device: one
+// thread per sequence restarts its sum where a head recomputed this step and
+// adds this step's count where all reused.  No launch of the same step reads
+// the sums after this one.
+__device__ __forceinline__ void update_cum(const AttnParams& p, int b, int g, int rt) {
+  if (p.cum == nullptr || g != 0 || rt != 0 || threadIdx.x != 0) return;
+  bool any = false;
+  for (int h = 0; h < p.hq; ++h) any |= head_selected(p.sel, b, b * p.hq + h);
+  p.cum[b] = any ? 0 : p.cum[b] + p.cum_m[b];
 }
 
 // Groups (sequence, kv head) with at least one selected query head, as a bit

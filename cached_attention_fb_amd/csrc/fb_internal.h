@@ -20,11 +20,17 @@ constexpr int combine_rows(int head_dim) { return 4 * kCombineThreads / head_dim
 
 // Which heads a launch works on.  A head (b, h) is selected when bit b of
 // `seq_bits` is set and, if `flags` is not null, (flags[b*Hq+h] != 0) equals
-// `flags_select`.
+// `flags_select`; or, if `m` is not null (threshold decided on the device),
+// unless the head holds a computed A_out (valid) and m[b] (+ cum[b] when cum
+// is not null) < tau.  m, cum and valid must not change during the launch.
 struct HeadSel {
   uint32_t seq_bits[FB_MAX_BATCH / 32];
   const uint8_t* flags;
   int32_t flags_select;
+  int32_t tau;
+  const int32_t* m;       // [B] updated tokens of this step
+  const int32_t* cum;     // [B] sums since the last computation (cumulative rule) or null
+  const uint8_t* valid;   // [B][Hq]
 };
 
 // Split plan chosen on the device (per-head decisions made on the device,
@@ -68,7 +74,13 @@ struct AttnParams {
   const uint8_t* cur;     // [B][Hq] current slot
   const uint8_t* valid;   // [B][Hq]
   void* out;              // [B][Hq][Bs][D]
-  uint8_t* reuse_rec;     // [B][Hq] or null: 1 - selected(b, h) is recorded
+  // [B][Hq] or null: 1 - selected(b, h) is recorded (merge: by the head's own
+  // rows; partial: every head, by the first workgroup, for the launches after)
+  uint8_t* reuse_rec;
+  // merge, cumulative threshold on the device: cum[b] restarts at 0 when a
+  // head of b was selected (recomputed), else grows by m[b]
+  int32_t* cum;
+  const int32_t* cum_m;
 };
 
 struct CombineParams {
@@ -102,6 +114,8 @@ struct DecideParams {
 
 struct ResetParams {
   int32_t n_heads;
+  int32_t batch;
+  int32_t* cum;           // [B] or null
   uint8_t* cur;
   uint8_t* valid;
   uint8_t* reuse;         // [2][B*Hq]

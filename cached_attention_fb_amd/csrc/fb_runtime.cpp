@@ -89,10 +89,12 @@ struct fb_cache {
   float* part_o = nullptr;   // [splits_cap][B][Hq][Bs][D]
   float* part_l = nullptr;   // [splits_cap][B][Hq][Bs]
   float* cos_part = nullptr; // [B][Hq][row_chunks][3]
+  int32_t* cum = nullptr;    // [B] cumulative rule decided on the device: updated tokens since b's last computation
   // host state
   int64_t steps = 0;         // fb_step calls since the last reset
   int32_t block_prefix = -1; // prefix_len of the current block
   int32_t block_policy = -1;
+  int32_t block_dev_m = -1;  // 1: the block's threshold decisions are made on the device
   std::vector<uint8_t> host_valid;   // [B]: every head of b holds a computed A_out (tau bookkeeping)
   std::vector<int64_t> cum_updated;  // [B]: TAU_CUM, updated tokens summed since b's last computation
   // profiling
@@ -160,6 +162,16 @@ int choose_splits(const fb_cache* c, int n_keys, int active_groups) {
   return (tiles + tiles_per - 1) / tiles_per;   // no empty chunk
 }
 
+// Profiling records HIP events, which stream capture would take into a graph.
+fb_status check_not_capturing_profiled(const fb_cache* c, hipStream_t s) {
+  if (!c->prof) return FB_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return hip_fail(e, "stream capture query");
+  if (cs != hipStreamCaptureStatusNone) return fail(FB_E_STATE, "profiling is on while the stream is being captured");
+  return FB_OK;
+}
+
 void prof_begin(fb_cache* c, hipStream_t s, ProfRec* r, int kind) {
   r->kind = -1;
   if (!c->prof) return;
@@ -224,8 +236,12 @@ fbk::AttnParams attn_common(const fb_cache* c, const void* q, int waves, int ksp
   return p;
 }
 
+// External attention over prefix rows 0..n-1 for the heads `sel` selects, and
+// the split combine into the cache.  rec != null: the attention launch records
+// its per-head decisions there and the combine selects from that record.
 fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* vp, int32_t n,
-                       const fbk::HeadSel& sel, int active_groups, bool gamma, hipStream_t s) {
+                       const fbk::HeadSel& sel, int active_groups, bool gamma, hipStream_t s,
+                       uint8_t* rec = nullptr) {
   fbk::AttnParams p = attn_common(c, q, c->ext_waves, c->ext_ksplit);
   p.k = kp;
   p.v = vp;
@@ -234,13 +250,21 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   p.splits = choose_splits(c, n, active_groups);
   const int tiles = (n + fbk::kKeyTile - 1) / fbk::kKeyTile;
   p.keys_per_split = std::max(1, (tiles + p.splits - 1) / p.splits) * fbk::kKeyTile;
-  if (sel.flags != nullptr && dyn_possible(c) && n > 0) {
+  if ((sel.flags != nullptr || sel.m != nullptr) && dyn_possible(c) && n > 0) {
     plan_dyn(c, n);   // heads chosen on the device: the split count follows how many groups it selects
     p.dyn = c->dyn;
     p.grid = c->dyn_grid;
     p.keys_per_split = c->dyn_kps;   // the longest range the plan may pick (LDS sizing)
+  } else if (sel.flags == nullptr && sel.m == nullptr && dyn_possible(c) && n > 0 &&
+             active_groups < c->cfg.batch * c->cfg.n_kv_heads) {
+    // some sequences chosen on the host: enumerate only their groups, so the
+    // work spreads over every XCD instead of the slice of the grid they own
+    plan_dyn(c, n);
+    p.dyn = c->dyn;
+    p.grid = active_groups * p.row_tiles * p.splits;   // p.splits == dyn.splits[active_groups]
   }
   p.sel = sel;
+  p.reuse_rec = rec;
   p.part_o = c->part_o;
   p.part_l = c->part_l;
   p.part_o_stride = elems_per_slot(c->cfg);
@@ -264,6 +288,11 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   cp.bs = c->cfg.block_size;
   cp.row_chunks = c->row_chunks;
   cp.sel = sel;
+  if (rec != nullptr) {
+    cp.sel = all_heads(c);
+    cp.sel.flags = rec;
+    cp.sel.flags_select = 0;
+  }
   cp.slot_o = c->slot_o;
   cp.slot_l = c->slot_l;
   cp.slot_o_stride = elems_per_slot(c->cfg);
@@ -280,7 +309,8 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
 }
 
 fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* vb, void* out,
-                       const fbk::HeadSel& rec_sel, uint8_t* reuse_rec, hipStream_t s) {
+                       const fbk::HeadSel& rec_sel, uint8_t* reuse_rec, hipStream_t s,
+                       const int32_t* cum_m = nullptr) {
   fbk::AttnParams p = attn_common(c, q, c->int_waves, c->int_ksplit);
   p.k = kb;
   p.v = vb;
@@ -297,6 +327,10 @@ fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* v
   p.valid = c->valid;
   p.out = out;
   p.reuse_rec = reuse_rec;
+  if (cum_m != nullptr) {
+    p.cum = c->cum;
+    p.cum_m = cum_m;
+  }
   ProfRec r;
   prof_begin(c, s, &r, 2);
   hipError_t e = fbk::launch_attn(c->cfg.dtype, c->cfg.head_dim, fbk::kModeMerge, p, s);
@@ -308,6 +342,8 @@ fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* v
 fb_status run_reset(fb_cache* c, hipStream_t s) {
   fbk::ResetParams rp{};
   rp.n_heads = c->cfg.batch * c->cfg.n_q_heads;
+  rp.batch = c->cfg.batch;
+  rp.cum = c->cum;
   rp.cur = c->cur;
   rp.valid = c->valid;
   rp.reuse = c->reuse;
@@ -320,13 +356,14 @@ fb_status run_reset(fb_cache* c, hipStream_t s) {
   c->steps = 0;
   c->block_prefix = -1;
   c->block_policy = -1;
+  c->block_dev_m = -1;
   std::fill(c->host_valid.begin(), c->host_valid.end(), 0);
   std::fill(c->cum_updated.begin(), c->cum_updated.end(), 0);
   return FB_OK;
 }
 
 void free_all(fb_cache* c) {
-  void* ptrs[] = {c->slot_o, c->slot_l, c->cur, c->valid, c->reuse, c->sim, c->part_o, c->part_l, c->cos_part};
+  void* ptrs[] = {c->slot_o, c->slot_l, c->cur, c->valid, c->reuse, c->sim, c->part_o, c->part_l, c->cos_part, c->cum};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& r : c->prof_recs) {
@@ -408,6 +445,7 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
       {(void**)&c->part_o, (size_t)c->splits_cap * so},
       {(void**)&c->part_l, (size_t)c->splits_cap * sl},
       {(void**)&c->cos_part, (size_t)nh * c->row_chunks * 3 * sizeof(float)},
+      {(void**)&c->cum, (size_t)cfg->batch * sizeof(int32_t)},
   };
   for (auto& a : plan) {
     e = hipMalloc(a.p, std::max<size_t>(a.n, 256));
@@ -446,6 +484,7 @@ fb_status fb_cache_reset(fb_cache* c, void* stream) {
   if (!c) return fail(FB_E_ARG, "cache is null");
   DeviceGuard g(c->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "set device");
+  if (fb_status pst = check_not_capturing_profiled(c, (hipStream_t)stream); pst != FB_OK) return pst;
   fb_status st = run_reset(c, (hipStream_t)stream);
   return st == FB_OK ? ok() : st;
 }
@@ -502,15 +541,20 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   // sequences whose heads recompute the external part (TAU decides per sequence)
   fbk::HeadSel sel{};
   int active = 0;
+  const bool dev_m = tau_like && pa->n_updated_dev != nullptr;
   if (tau_like) {
     if (pa->tau < 0) return fail(FB_E_ARG, "tau %d is negative", pa->tau);
-    if (!pa->n_updated) return fail(FB_E_ARG, "n_updated is null under the tau policy");
-    for (int b = 0; b < B; ++b)
-      if (pa->n_updated[b] < 0) return fail(FB_E_ARG, "n_updated[%d] = %d is negative", b, pa->n_updated[b]);
+    if (!pa->n_updated && !pa->n_updated_dev) return fail(FB_E_ARG, "n_updated and n_updated_dev are null under the tau policy");
+    if (pa->n_updated && pa->n_updated_dev) return fail(FB_E_ARG, "both n_updated and n_updated_dev are set");
+    if (!dev_m)
+      for (int b = 0; b < B; ++b)
+        if (pa->n_updated[b] < 0) return fail(FB_E_ARG, "n_updated[%d] = %d is negative", b, pa->n_updated[b]);
   }
+  if (c->steps > 0 && (dev_m ? 1 : 0) != c->block_dev_m)
+    return fail(FB_E_STATE, "decisions moved between host and device inside a block (reset first)");
   if (gamma_like && !(pa->gamma == pa->gamma)) return fail(FB_E_ARG, "gamma is NaN");
   std::vector<uint8_t> reuse_seq(B, 0);
-  for (int b = 0; b < B; ++b) {
+  for (int b = 0; b < B && !dev_m; ++b) {
     bool reuse = false;
     if (pa->policy == FB_POLICY_TAU) reuse = c->host_valid[b] && pa->n_updated[b] < pa->tau;
     if (pa->policy == FB_POLICY_TAU_CUM) reuse = c->host_valid[b] && c->cum_updated[b] + pa->n_updated[b] < pa->tau;
@@ -523,6 +567,7 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   DeviceGuard g(c->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "set device");
   hipStream_t s = (hipStream_t)stream;
+  if (fb_status pst = check_not_capturing_profiled(c, s); pst != FB_OK) return pst;
   const int64_t nh = (int64_t)B * c->cfg.n_q_heads;
   uint8_t* reuse_now = c->reuse + (c->steps & 1) * nh;
   uint8_t* reuse_next = c->reuse + ((c->steps + 1) & 1) * nh;
@@ -552,6 +597,21 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
     prof_end(c, s, &r);
     if (e != hipSuccess) return hip_fail(e, "decision launch");
     st = run_internal(c, q_blk, k_blk, v_blk, out, sel, nullptr, s);
+  } else if (dev_m) {
+    // threshold decided in the external launch from the counts in device
+    // memory; it records the decisions, the later launches follow them
+    sel = all_heads(c);
+    sel.m = pa->n_updated_dev;
+    sel.tau = pa->tau;
+    sel.valid = c->valid;
+    sel.cum = pa->policy == FB_POLICY_TAU_CUM ? c->cum : nullptr;
+    st = run_external(c, q_blk, k_prefix, v_prefix, prefix_len, sel, B * c->cfg.n_kv_heads, false, s, reuse_now);
+    if (st != FB_OK) return st;
+    fbk::HeadSel rec = all_heads(c);
+    rec.flags = reuse_now;
+    rec.flags_select = 0;
+    st = run_internal(c, q_blk, k_blk, v_blk, out, rec, nullptr, s,
+                      pa->policy == FB_POLICY_TAU_CUM ? pa->n_updated_dev : nullptr);
   } else {
     sel.flags = nullptr;
     sel.flags_select = 1;
@@ -570,6 +630,7 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   if (c->steps == 0) {
     c->block_prefix = prefix_len;
     c->block_policy = pa->policy;
+    c->block_dev_m = dev_m ? 1 : 0;
   }
   c->steps += 1;
   return ok();

@@ -39,7 +39,7 @@ class FBConfig(ctypes.Structure):
 
 class FBPolicyArgs(ctypes.Structure):
     _fields_ = [("policy", ctypes.c_int32), ("tau", ctypes.c_int32), ("gamma", ctypes.c_float),
-                ("n_updated", ctypes.POINTER(ctypes.c_int32))]
+                ("n_updated", ctypes.POINTER(ctypes.c_int32)), ("n_updated_dev", ctypes.c_void_p)]
 
 
 class FBProfileStats(ctypes.Structure):
@@ -157,9 +157,19 @@ class Cache:
                                                _stream(stream)))
 
     def step(self, policy: int, q, k_blk, v_blk, k_prefix, v_prefix, prefix_len: int, out,
-             tau: int = 0, gamma: float = 0.0, n_updated=None, stream=None) -> None:
-        args = FBPolicyArgs(policy, tau, gamma, None)
+             tau: int = 0, gamma: float = 0.0, n_updated=None, n_updated_dev=None, stream=None) -> None:
+        """One denoising step.  Threshold counts come either from the host
+        (`n_updated`, B ints) or from device memory (`n_updated_dev`, an int32
+        tensor of B entries on the cache's device), in which case the
+        decisions are made on the device."""
+        args = FBPolicyArgs(policy, tau, gamma, None, None)
         keep = None
+        if n_updated_dev is not None:
+            if (not isinstance(n_updated_dev, torch.Tensor) or n_updated_dev.dtype != torch.int32
+                    or not n_updated_dev.is_cuda or n_updated_dev.numel() != self.cfg.batch
+                    or not n_updated_dev.is_contiguous()):
+                raise ValueError(f"n_updated_dev must be a contiguous int32 device tensor of {self.cfg.batch} entries")
+            args.n_updated_dev = n_updated_dev.data_ptr()
         if n_updated is not None:
             keep = np.ascontiguousarray(np.asarray(n_updated, dtype=np.int32).reshape(-1))
             if keep.size != self.cfg.batch:
@@ -222,17 +232,26 @@ class PreparedStep:
         self.ptrs = (q, kb, vb, kp, vp)
         self.out = out
         self.m = (ctypes.c_int32 * cache.cfg.batch)()
-        self.args = FBPolicyArgs(0, 0, 0.0, ctypes.cast(self.m, ctypes.POINTER(ctypes.c_int32)))
+        self.m_ptr = ctypes.cast(self.m, ctypes.POINTER(ctypes.c_int32))
+        self.args = FBPolicyArgs(0, 0, 0.0, self.m_ptr, None)
         self.args_ref = ctypes.byref(self.args)
         self.fn = cache.lib.fb_step
 
     def __call__(self, policy: int, prefix_len: int, n_updated=None, tau: int = 0, gamma: float = 0.0,
-                 stream=None) -> None:
+                 stream=None, n_updated_dev: Optional[int] = None) -> None:
+        """n_updated_dev: device address of B int32 counts (decisions on the
+        device); n_updated is then ignored."""
         a = self.args
         a.policy, a.tau, a.gamma = policy, tau, gamma
-        if n_updated is not None:
-            for i, v in enumerate(n_updated):
-                self.m[i] = int(v)
+        if n_updated_dev is not None:
+            a.n_updated = None
+            a.n_updated_dev = n_updated_dev
+        else:
+            a.n_updated = self.m_ptr
+            a.n_updated_dev = None
+            if n_updated is not None:
+                for i, v in enumerate(n_updated):
+                    self.m[i] = int(v)
         q, kb, vb, kp, vp = self.ptrs
         code = self.fn(self.cache.h, self.args_ref, q, kb, vb, kp, vp, prefix_len, self.out,
                        _stream(stream) if stream is None or not isinstance(stream, int) else stream)

@@ -145,6 +145,13 @@ typedef struct {
                                 group's similarity */
   const int32_t* n_updated;  /* host int32 [B]: tokens of the block updated since the
                                 previous step (TAU, TAU_CUM; ignored otherwise) */
+  const int32_t* n_updated_dev;
+                             /* device int32 [B], values >= 0 (not checked): the same
+                                counts in device memory, read by the step's kernels when
+                                they run; the decisions are then made on the device, per
+                                head, from each head's own valid flag.  Exactly one of
+                                n_updated and n_updated_dev is set under TAU/TAU_CUM; a
+                                block keeps the same choice until its reset. */
 } fb_policy_args;
 
 /* One denoising step (page §2): decide per head whether to reuse the cached
@@ -154,10 +161,23 @@ typedef struct {
  * decide its reuse at the next step; compute block-internal attention and the
  * merge into `out`.  The first step after a reset recomputes every head, and
  * under GAMMA so does the second (a similarity needs two computed A_out).
- * The whole step is asynchronous on `stream` (GAMMA decisions stay on the
- * device).  Errors: FB_E_ARG (null, bad policy, tau < 0, n_updated missing or
- * negative), FB_E_SHAPE, FB_E_STATE (prefix_len differs from the previous
- * step of the same block). */
+ * The whole step is asynchronous on `stream` (GAMMA decisions and TAU
+ * decisions from n_updated_dev stay on the device).  Errors: FB_E_ARG (null,
+ * bad policy, tau < 0, neither or both of n_updated / n_updated_dev under TAU,
+ * a negative n_updated), FB_E_SHAPE, FB_E_STATE (prefix_len, policy or the
+ * host/device choice differs from the previous step of the same block).
+ *
+ * Graph capture: fb_step and fb_cache_reset enqueue kernel launches only (no
+ * copy, memset, allocation or synchronisation) and, when no decision is made
+ * on the host (ALWAYS, GAMMA, GAMMA_GROUP, or TAU/TAU_CUM with
+ * n_updated_dev), nothing they enqueue depends on device values read by the
+ * host, so they may be recorded by HIP stream capture with profiling off.  A
+ * replay repeats the launches as recorded, host choices included (the step's
+ * position in its block, prefix_len, pointers such as n_updated_dev), so a
+ * graph holds whole blocks, each starting with fb_cache_reset; between replays
+ * the caller may change the contents of the buffers, not their addresses.
+ * With profiling on, fb_step and fb_cache_reset on a capturing stream return
+ * FB_E_STATE. */
 fb_status fb_step(fb_cache* c, const fb_policy_args* p, const void* q_blk, const void* k_blk,
                   const void* v_blk, const void* k_prefix, const void* v_prefix,
                   int32_t prefix_len, void* out, void* stream);

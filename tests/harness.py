@@ -72,8 +72,10 @@ def device_prefix(inp: wl.Inputs, max_prefix: int, dev="cuda") -> Tuple[torch.Te
 
 
 def run_gpu(inp: wl.Inputs, policy: Optional[str] = None, kv_splits: int = 0,
-            record_cache: bool = True) -> List[GpuBlock]:
-    """All blocks of ``inp`` through fb_step, block K/V appended at block end."""
+            record_cache: bool = True, device_counts: bool = False) -> List[GpuBlock]:
+    """All blocks of ``inp`` through fb_step, block K/V appended at block end.
+    device_counts: the threshold counts are passed in device memory (the
+    decisions are then made by the kernels)."""
     w = inp.workload
     policy = policy or w.policy
     n0 = inp.k_prefix.shape[2]
@@ -85,6 +87,7 @@ def run_gpu(inp: wl.Inputs, policy: Optional[str] = None, kv_splits: int = 0,
     kb = torch.empty((w.batch, w.n_kv_heads, w.block, w.head_dim), dtype=dt, device="cuda")
     vb = torch.empty_like(kb)
     out = torch.empty_like(q)
+    m_dev = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
     n = n0
     res = []
     for blk in inp.blocks:
@@ -98,8 +101,13 @@ def run_gpu(inp: wl.Inputs, policy: Optional[str] = None, kv_splits: int = 0,
             q.copy_(st.q)
             kb.copy_(st.k)
             vb.copy_(st.v)
-            cache.step(POLICY_CODE[policy], q, kb, vb, kp, vp, n, out, tau=w.tau, gamma=w.gamma,
-                       n_updated=st.n_updated)
+            if device_counts:
+                m_dev.copy_(torch.as_tensor(np.asarray(st.n_updated, dtype=np.int32)))
+                cache.step(POLICY_CODE[policy], q, kb, vb, kp, vp, n, out, tau=w.tau, gamma=w.gamma,
+                           n_updated_dev=m_dev)
+            else:
+                cache.step(POLICY_CODE[policy], q, kb, vb, kp, vp, n, out, tau=w.tau, gamma=w.gamma,
+                           n_updated=st.n_updated)
             g.out[s] = out.to(torch.float64).cpu().numpy()
             g.reuse[s] = cache.read(fb.FIELD_REUSE)
             if record_cache:
