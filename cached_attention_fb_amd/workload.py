@@ -202,6 +202,30 @@ def generate(w: Workload, seed: Optional[int] = None, prefix: Optional[int] = No
     return Inputs(w, seed, k_pre, v_pre, blocks)
 
 
+SPARSE_TILE = 64   # prefix keys per selectable tile
+
+
+def sparse_selection(w: Workload, n_prefix: int, density: float, seed: Optional[int] = None) -> np.ndarray:
+    """A synthetic sparse-attention selection (standing in for a selector such
+    as SparseD, which is not part of this package): for every (sequence,
+    key/value head), round(density * tiles) of the prefix's 64-key tiles
+    (at least one when the prefix is not empty), always the most recent one
+    plus tiles drawn uniformly without replacement; ascending, int32
+    [B, Hkv, n_sel].  Drawn from its own generator so the other inputs do not
+    depend on it."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 7919)
+    tiles = (n_prefix + SPARSE_TILE - 1) // SPARSE_TILE
+    n_sel = 0 if tiles == 0 else min(tiles, max(1, int(round(density * tiles))))
+    sel = np.zeros((w.batch, w.n_kv_heads, n_sel), dtype=np.int32)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            if n_sel == 0:
+                continue
+            others = rng.choice(tiles - 1, size=n_sel - 1, replace=False) if n_sel > 1 else np.zeros(0, int)
+            sel[b, g] = np.sort(np.concatenate([others, [tiles - 1]]))
+    return sel
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a working-dtype tensor to a float64 numpy array."""
     return t.to(torch.float64).numpy()

@@ -6,8 +6,8 @@ with the HIP path and imports nothing from it.
 """
 from .flashblock import (ALWAYS, GAMMA, GAMMA_GROUP, TAU, TAU_CUM, BlockResult, HeadState, StepData, attend,
                          cosine, decide, default_scale, external, internal_merge, merge,
-                         run_block, run_blocks)
+                         run_block, run_block_sparse, run_blocks, SPARSE_TILE, tile_rows)
 
 __all__ = ["ALWAYS", "GAMMA", "GAMMA_GROUP", "TAU", "TAU_CUM", "BlockResult", "HeadState", "StepData", "attend",
            "cosine", "decide", "default_scale", "external", "internal_merge", "merge",
-           "run_block", "run_blocks"]
+           "run_block", "run_block_sparse", "run_blocks", "SPARSE_TILE", "tile_rows"]

@@ -19,6 +19,10 @@ What is computed, step by step, for every (sequence b, query head h):
 * ``cosine`` — per-head similarity of two A_out tensors (§2 "Sélection par
   tête"; the measure itself is not named on the page, cosine is the reading
   taken here).
+* ``run_block_sparse`` — the same policy over a sparse attention (§2
+  "Compatibilité avec l'attention parcimonieuse"): the prefix keys a
+  selection leaves out form the cached external set, the kept ones are
+  attended afresh at every step.
 * ``decide`` / ``run_block`` — the reuse policy (§2 "Réutilisation basée sur
   un seuil": reuse when M^{s+1} < tau, else recompute; "Sélection par tête":
   only heads whose similarity exceeds gamma reuse) driving one block of
@@ -234,6 +238,90 @@ def run_block(k_prefix: np.ndarray, v_prefix: np.ndarray, n_prefix: int,
             for st, (_, h) in zip(sts, unit):
                 a_in, l_in = attend(step.q[b, h], step.k[b, g], step.v[b, g], scale)
                 out[s, b, h], _ = merge(st.a_out, st.l_out, a_in, l_in)
+                a_rec[s, b, h] = st.a_out
+                l_rec[s, b, h] = st.l_out
+                reuse[s, b, h] = 1 if r else 0
+                sim[s, b, h] = np.nan if st.sim is None else st.sim
+    return BlockResult(out, a_rec, l_rec, reuse, sim)
+
+
+SPARSE_TILE = 64   # prefix keys per selectable tile (the selection's granularity)
+
+
+def tile_rows(tiles: Sequence[int], n_prefix: int, tile: int = SPARSE_TILE) -> np.ndarray:
+    """Prefix rows of the listed key tiles (tile t holds rows tile*t ..
+    tile*t + tile - 1, cut at n_prefix), ascending."""
+    rows = [np.arange(t * tile, min((t + 1) * tile, n_prefix)) for t in sorted(set(int(t) for t in tiles))]
+    return np.concatenate(rows).astype(np.int64) if rows else np.zeros(0, np.int64)
+
+
+def sparse_key_sets(tiles: Sequence[int], n_prefix: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Prefix rows kept by a selection of tiles, and the rows it leaves out
+    (the rest of 0..n_prefix-1); together they cover the prefix once."""
+    kept = tile_rows(tiles, n_prefix)
+    return kept, np.setdiff1d(np.arange(n_prefix), kept)
+
+
+def run_block_sparse(k_prefix: np.ndarray, v_prefix: np.ndarray, n_prefix: int,
+                     steps: Sequence[StepData], sel_tiles: np.ndarray, policy: str, tau: int = 0,
+                     gamma: float = 0.0, scale: Optional[float] = None,
+                     heads: Optional[Iterable[Tuple[int, int]]] = None) -> BlockResult:
+    """FlashBlock over a sparse attention (§2 "Compatibilité avec l'attention
+    parcimonieuse", §3 item 3): the prefix keys a sparse selection keeps are
+    attended afresh at every step; the keys it leaves out play the role of the
+    block-external set, whose part (A_res, L_res) is cached and reused under
+    the policy exactly as A_out/L_out are in ``run_block``.
+
+    ``sel_tiles`` [B, Hkv, n_sel]: the kept prefix tiles of each (sequence,
+    key/value head), shared by the query heads that read that key/value head,
+    and fixed for the block.  Per step and head: decide reuse of the residual;
+    if not reused, A_res, L_res = attend over the left-out rows (similarity
+    under gamma measured on A_res); A_sel, L_sel = attend over the kept rows;
+    A_in, L_in = attend over the block; output = merge(merge(residual, kept),
+    internal).  With no kept tile this is ``run_block``; with every tile kept
+    the residual is empty and every step is exact attention.  Records: out,
+    the cached residual (a_out, l_out), reuse, sim."""
+    s0 = steps[0]
+    n_steps = len(steps)
+    bsz, hq, bs, d = s0.q.shape
+    hkv = s0.k.shape[1]
+    group = hq // hkv
+    scale = default_scale(d) if scale is None else scale
+    heads = [(b, h) for b in range(bsz) for h in range(hq)] if heads is None else list(heads)
+    out = np.full((n_steps, bsz, hq, bs, d), np.nan)
+    a_rec = np.full((n_steps, bsz, hq, bs, d), np.nan)
+    l_rec = np.full((n_steps, bsz, hq, bs), np.nan)
+    reuse = np.full((n_steps, bsz, hq), -1, dtype=np.int8)
+    sim = np.full((n_steps, bsz, hq), np.nan)
+    if policy == GAMMA_GROUP:
+        units = [[(b, g * group + i) for i in range(group)] for b, g in sorted({(b, h // group) for b, h in heads})]
+    else:
+        units = [[bh] for bh in heads]
+    for unit in units:
+        b, g = unit[0][0], unit[0][1] // group
+        kept, left = sparse_key_sets(sel_tiles[b, g], n_prefix)
+        k_kept, v_kept = k_prefix[b, g, kept], v_prefix[b, g, kept]
+        k_left, v_left = k_prefix[b, g, left], v_prefix[b, g, left]
+        sts = [HeadState() for _ in unit]
+        for s, step in enumerate(steps):
+            m = int(step.n_updated[b])
+            r = decide(policy, sts[0], m, tau, gamma)
+            if not r:
+                news = [attend(step.q[b, h], k_left, v_left, scale) for _, h in unit]
+                if policy in (GAMMA, GAMMA_GROUP) and sts[0].valid:
+                    sim_u = cosine(np.stack([a for a, _ in news]), np.stack([st.a_out for st in sts]))
+                    for st in sts:
+                        st.sim = sim_u
+                for st, (a_new, l_new) in zip(sts, news):
+                    st.a_out, st.l_out, st.valid, st.cum = a_new, l_new, True, 0
+            else:
+                for st in sts:
+                    st.cum += m
+            for st, (_, h) in zip(sts, unit):
+                a_sel, l_sel = attend(step.q[b, h], k_kept, v_kept, scale)
+                a_ext, l_ext = merge(st.a_out, st.l_out, a_sel, l_sel)
+                a_in, l_in = attend(step.q[b, h], step.k[b, g], step.v[b, g], scale)
+                out[s, b, h], _ = merge(a_ext, l_ext, a_in, l_in)
                 a_rec[s, b, h] = st.a_out
                 l_rec[s, b, h] = st.l_out
                 reuse[s, b, h] = 1 if r else 0

@@ -395,10 +395,121 @@ def pin_gamma_group_policy():
     assert np.array_equal(np.nan_to_num(a.sim, nan=-9), np.nan_to_num(bres.sim, nan=-9))
 
 
+# ---------------------------------------------------------------- sparse residual reuse
+
+def _sdpa_rows(q, k, v):
+    """torch's float64 scaled-dot-product attention of rows q over keys k."""
+    t = lambda x: torch.as_tensor(np.asarray(x, np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0, 0].numpy()
+
+
+def _sparse_setup(seed, n=150, b=2, hq=4, hkv=2, bs=8, d=16, m_list=None):
+    rng = _rng(seed)
+    kp, vp = rng.standard_normal((b, hkv, n, d)), rng.standard_normal((b, hkv, n, d))
+    m_list = m_list or [[0] * b, [2] * b, [8] * b, [1] * b]
+    steps = _steps(rng, b, hq, hkv, bs, d, m_list)
+    return rng, kp, vp, steps
+
+
+def pin_sparse_always_is_exact():
+    """Recomputing the residual every step gives exact attention over the whole
+    prefix and the block, whatever the selection (kept + left = prefix)."""
+    rng, kp, vp, steps = _sparse_setup(30)
+    n, tiles = kp.shape[2], 3                      # tiles 0, 1 and a ragged tile 2 (22 rows)
+    for sel in (np.array([[[2], [0]], [[1], [2]]]), np.array([[[0, 2], [1, 2]], [[0, 1], [0, 2]]])):
+        res = fb.run_block_sparse(kp, vp, n, steps, sel, fb.ALWAYS)
+        for s, st in enumerate(steps):
+            for bi in range(2):
+                for h in range(4):
+                    g = h // 2
+                    ref = _sdpa_rows(st.q[bi, h], np.concatenate([kp[bi, g], st.k[bi, g]]),
+                                     np.concatenate([vp[bi, g], st.v[bi, g]]))
+                    assert np.max(np.abs(res.out[s, bi, h] - ref)) < 1e-12
+        assert np.all(res.reuse == 0)
+
+
+def pin_sparse_all_kept_is_exact():
+    """With every tile kept the residual is empty (L = -inf), so even steps
+    that reuse it are exact attention."""
+    rng, kp, vp, steps = _sparse_setup(31)
+    sel = np.tile(np.arange(3), (2, 2, 1))
+    res = fb.run_block_sparse(kp, vp, kp.shape[2], steps, sel, fb.TAU, tau=4)
+    assert res.reuse[1:].any()
+    assert np.all(np.isneginf(res.l_out))
+    for s, st in enumerate(steps):
+        for bi in range(2):
+            for h in range(4):
+                g = h // 2
+                ref = _sdpa_rows(st.q[bi, h], np.concatenate([kp[bi, g], st.k[bi, g]]),
+                                 np.concatenate([vp[bi, g], st.v[bi, g]]))
+                assert np.max(np.abs(res.out[s, bi, h] - ref)) < 1e-12
+
+
+def pin_sparse_none_kept_is_flashblock():
+    """With no tile kept the method is FlashBlock itself: every record equals
+    run_block's bit for bit (merging an empty part changes nothing)."""
+    rng, kp, vp, steps = _sparse_setup(32)
+    sel = np.zeros((2, 2, 0), np.int64)
+    for pol, kw in ((fb.TAU, {"tau": 4}), (fb.GAMMA, {"gamma": 0.5})):
+        a = fb.run_block_sparse(kp, vp, kp.shape[2], steps, sel, pol, **kw)
+        r = fb.run_block(kp, vp, kp.shape[2], steps, pol, **kw)
+        for f in ("out", "a_out", "l_out", "reuse"):
+            assert np.array_equal(getattr(a, f), getattr(r, f)), f
+        assert np.array_equal(np.nan_to_num(a.sim, nan=-9), np.nan_to_num(r.sim, nan=-9))
+
+
+def pin_sparse_stale_residual_bruteforce():
+    """A reused residual is the left-out keys' contribution for the query of
+    the step that computed it: scalar brute force over two steps (the second
+    reuses), with the kept tile the ragged last one."""
+    rng = _rng(33)
+    n, bs, d = 70, 3, 4
+    kp, vp = rng.standard_normal((1, 1, n, d)), rng.standard_normal((1, 1, n, d))
+    steps = _steps(rng, 1, 1, 1, bs, d, [[0], [3]])
+    sel = np.array([[[1]]])                       # keeps rows 64..69, leaves 0..63
+    res = fb.run_block_sparse(kp, vp, n, steps, sel, fb.TAU, tau=100)
+    assert list(res.reuse[:, 0, 0]) == [0, 1]
+    c = 1.0 / math.sqrt(d)
+    q1, st2 = steps[0].q[0, 0], steps[1]
+    for i in range(bs):
+        num, den = [0.0] * d, 0.0
+        terms = [(st2.q[0, 0, i], kp[0, 0, j], vp[0, 0, j]) for j in range(64, n)]
+        terms += [(st2.q[0, 0, i], st2.k[0, 0, j], st2.v[0, 0, j]) for j in range(bs)]
+        terms += [(q1[i], kp[0, 0, j], vp[0, 0, j]) for j in range(64)]   # stale: the first step's query
+        for qi, kj, vj in terms:
+            w = math.exp(c * sum(float(qi[t]) * float(kj[t]) for t in range(d)))
+            den += w
+            num = [num[t] + w * float(vj[t]) for t in range(d)]
+        assert np.max(np.abs(res.out[1, 0, 0, i] - np.array(num) / den)) < 1e-12
+
+
+def pin_sparse_gamma_on_residual():
+    """Under gamma the similarity is that of the residual part: scipy's cosine
+    of torch's attention over the left-out rows for two consecutive queries."""
+    rng, kp, vp, steps = _sparse_setup(34, m_list=[[0] * 2, [3] * 2, [3] * 2])
+    sel = np.array([[[1], [0, 2]], [[2], [1]]], dtype=object)
+    sel = [[np.array(x) for x in row] for row in sel]
+    sel_arr = np.empty((2, 2), dtype=object)
+    for i in range(2):
+        for j in range(2):
+            sel_arr[i, j] = sel[i][j]
+    res = fb.run_block_sparse(kp, vp, kp.shape[2], steps, sel_arr, fb.GAMMA, gamma=0.99)
+    for bi in range(2):
+        for h in range(4):
+            g = h // 2
+            kept = {r for t in sel_arr[bi, g] for r in range(64 * t, min(64 * t + 64, kp.shape[2]))}
+            left = [r for r in range(kp.shape[2]) if r not in kept]
+            a1 = _sdpa_rows(steps[0].q[bi, h], kp[bi, g, left], vp[bi, g, left])
+            a2 = _sdpa_rows(steps[1].q[bi, h], kp[bi, g, left], vp[bi, g, left])
+            ref = 1.0 - scipy.spatial.distance.cosine(a2.ravel(), a1.ravel())
+            assert abs(res.sim[1, bi, h] - ref) < 1e-12
+
+
 PINS = [pin_attend_bruteforce, pin_attend_vs_torch, pin_external_gqa_vs_torch, pin_attend_closed_forms,
         pin_attend_permutation_invariance, pin_merge_equals_full_attention, pin_merge_special_cases,
         pin_split_associativity, pin_cosine, pin_tau_policy, pin_gamma_policy, pin_multi_block_append,
-        pin_tau_cum_policy, pin_gamma_group_policy]
+        pin_tau_cum_policy, pin_gamma_group_policy, pin_sparse_always_is_exact, pin_sparse_all_kept_is_exact,
+        pin_sparse_none_kept_is_flashblock, pin_sparse_stale_residual_bruteforce, pin_sparse_gamma_on_residual]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -510,6 +621,20 @@ def _external_mod_group(q, k_prefix, v_prefix, n_prefix, scale=None):
     return a, lse
 
 
+def _sparse_sets_shifted(tiles, n_prefix):
+    kept = np.array([r for t in sorted(set(int(t) for t in tiles)) for r in range(64 * t + 1, 64 * t + 65)
+                     if r < n_prefix], dtype=np.int64)
+    return kept, np.setdiff1d(np.arange(n_prefix), kept)
+
+
+def _sparse_sets_no_residual(tiles, n_prefix):
+    return fb.tile_rows(tiles, n_prefix), np.zeros(0, np.int64)
+
+
+def _sparse_sets_whole_prefix_left(tiles, n_prefix):
+    return fb.tile_rows(tiles, n_prefix), np.arange(n_prefix)
+
+
 MUTANTS = [
     ("attend", _attend_no_max_shift), ("attend", _attend_log2), ("attend", _attend_no_scale),
     ("attend", _attend_kv_swapped), ("attend", _attend_unnormalised),
@@ -518,6 +643,8 @@ MUTANTS = [
     ("cosine", _cosine_unclamped_l1), ("cosine", _cosine_no_abs), ("cosine", _cosine_mean_of_rows),
     ("decide", _decide_cum_le), ("decide", _decide_cum_per_step),
     ("external", _external_mod_group),
+    ("sparse_key_sets", _sparse_sets_shifted), ("sparse_key_sets", _sparse_sets_no_residual),
+    ("sparse_key_sets", _sparse_sets_whole_prefix_left),
 ]
 
 
@@ -533,3 +660,31 @@ def test_planted_mistakes(monkeypatch, name, mutant):
         except (AssertionError, FloatingPointError, ValueError, IndexError, TypeError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught the planted mistake {mutant.__name__}"
+
+
+def test_sparse_residual_recovers_dropped_keys():
+    """The pages' claim for sparse attention, on synthetic dLLM-shaped data:
+    caching the left-out keys' part (refreshed under the threshold policy)
+    brings the output far closer to exact attention than dropping those keys.
+    Sparse-only = attention over the kept tiles and the block alone."""
+    from cached_attention_fb_amd import workload as wl
+    w = wl.workload("dllm-8k").with_(n_q_heads=4, n_kv_heads=1, head_dim=32, steps=6)
+    inp = wl.generate(w, prefix=1024)
+    steps = [fb.StepData(wl.to_f64(st.q), wl.to_f64(st.k), wl.to_f64(st.v), np.asarray(st.n_updated))
+             for st in inp.blocks[0].steps]
+    kp, vp = wl.to_f64(inp.k_prefix), wl.to_f64(inp.v_prefix)
+    sel = wl.sparse_selection(w, 1024, 0.2)
+    exact = fb.run_block_sparse(kp, vp, 1024, steps, sel, fb.ALWAYS)
+    reuse = fb.run_block_sparse(kp, vp, 1024, steps, sel, fb.TAU, tau=w.tau)
+    assert reuse.reuse.sum() > 0
+    kept, _ = fb.sparse_key_sets(sel[0, 0], 1024)
+    scale = fb.default_scale(w.head_dim)
+    err_sparse = err_reuse = 0.0
+    for s, st in enumerate(steps):
+        for h in range(4):
+            a, l = fb.attend(st.q[0, h], kp[0, 0, kept], vp[0, 0, kept], scale)
+            a_in, l_in = fb.attend(st.q[0, h], st.k[0, 0], st.v[0, 0], scale)
+            only, _ = fb.merge(a, l, a_in, l_in)
+            err_sparse = max(err_sparse, np.max(np.abs(only - exact.out[s, 0, h])))
+            err_reuse = max(err_reuse, np.max(np.abs(reuse.out[s, 0, h] - exact.out[s, 0, h])))
+    assert err_reuse < 0.25 * err_sparse, (err_reuse, err_sparse)
