@@ -195,7 +195,7 @@ __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, c
     const int pos = ii * 64 + lane;                 // 16-byte slot inside the tile
     const int key = pos / P::kCpr, pc = pos % P::kCpr;
     const int swz = tensor == 0 ? (key & (P::kCpr - 1)) : ((4 * key) & (P::kCpr - 4));
-    const int gk = min(tile0 + key, key_end - 1);   // rows past the end: any valid row (masked later)
+    const int gk = max(0, min(tile0 + key, key_end - 1));   // rows past the end: any valid row (masked later)
     const bf16* src = (tensor == 0 ? kb : vb) + (int64_t)gk * D + (pc ^ swz) * 8;
     __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(stage + tensor * P::kTensorBytes + ii * 1024), 16, 0, 0);
   }
@@ -280,6 +280,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   const bf16* qg = reinterpret_cast<const bf16*>(p.q);
   const bf16* kb = reinterpret_cast<const bf16*>(p.k) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
   const bf16* vb = reinterpret_cast<const bf16*>(p.v) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
+  const TileMap tm = tile_map(p, b, g, key_begin, key_end);
+  const int lim = tm.lim;
 
   // Prologue loads, none waiting on another: the merge's head flags, then Q
   // and the first two tiles (more would only queue behind them in the memory
@@ -294,12 +296,12 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   if (kh == 0 && wave_live) issue_q<D>(q_lds, qg + (grow - rl) * D, p.rows - row0, lane);
   int issued;
   if (ntiles >= 2) {
-    issue_tile<D, WAVES>(lds, kb, vb, key_begin, key_end, wave, lane);
-    issue_tile<D, WAVES>(lds + P::kStageBytes, kb, vb, key_begin + kKeyTile, key_end, wave, lane);
+    issue_tile<D, WAVES>(lds, kb, vb, tm.key0(0), lim, wave, lane);
+    issue_tile<D, WAVES>(lds + P::kStageBytes, kb, vb, tm.key0(1), lim, wave, lane);
     issued = 2;
     wait_vmcnt<P::kLpt>();   // tile 0 (and everything issued before it) landed
   } else if (ntiles == 1) {
-    issue_tile<D, WAVES>(lds, kb, vb, key_begin, key_end, wave, lane);
+    issue_tile<D, WAVES>(lds, kb, vb, tm.key0(0), lim, wave, lane);
     issued = 1;
     wait_vmcnt<0>();
   } else {
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
       __builtin_amdgcn_s_barrier();   // every wave's share landed; all waves finished tile t_i-1
     }
     if (wave_live) {
-      const int tile0 = key_begin + t_i * kKeyTile;
+      const int tile0 = tm.key0(t_i);
       const uint32_t ks_off = lds_off + (t_i % P::kStages) * P::kStageBytes;
       const uint32_t vs_off = ks_off + P::kTensorBytes;
       // S^T, one 32-key half at a time: the half's K fragments in one batched
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) ka[t] = ks_off + k_off[t];
       f32x16 s[NH];
-      const int nh_live = (kShortSkip && tile0 + 32 >= key_end) ? 1 : NH;
+      const int nh_live = (kShortSkip && tile0 + 32 >= lim) ? 1 : NH;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         s[h] = f32x16{};
@@ -383,14 +385,14 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
         for (int t = 0; t < D / 16; ++t)
           s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[h], 0, 0, 0);
       }
-      // Ragged last tile: keys at or past key_end do not count.
+      // Ragged last tile: keys at or past the limit do not count.
       const int key0 = tile0 + 32 * kh * NH;
-      if (key0 + 32 * NH > key_end) {
+      if (key0 + 32 * NH > lim) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
 #pragma unroll
           for (int j = 0; j < 16; ++j)
-            if (key0 + 32 * h + 8 * (j >> 2) + 4 * hl + (j & 3) >= key_end) s[h][j] = -INFINITY;
+            if (key0 + 32 * h + 8 * (j >> 2) + 4 * hl + (j & 3) >= lim) s[h][j] = -INFINITY;
         }
       }
       // Row max of this wave's keys (log2 units); the running max is raised
@@ -444,8 +446,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     // Refill after the compute, so that a stalled issue does not delay it:
     // the stage of tile t_i-1 is free (every wave passed the barrier above).
     for (; issued < ntiles && issued <= t_i + P::kStages - 1; ++issued)
-      issue_tile<D, WAVES>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, key_begin + issued * kKeyTile,
-                           key_end, wave, lane);
+      issue_tile<D, WAVES>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, tm.key0(issued), lim, wave,
+                           lane);
   }
 
   if constexpr (KSPLIT == 2) {

@@ -72,13 +72,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
   for (int i = 0; i < kDt; ++i) o[i] = f32x16{};
   float m = -INFINITY, lsum = 0.0f;
 
+  const TileMap tm = tile_map(p, b, g, key_begin, key_end);
+  const int ntiles = key_end > key_begin ? (key_end - key_begin + kKeyTile - 1) / kKeyTile : 0;
   F32Tile<D> stage;
-  if (key_begin < key_end) stage.load(kb, vb, key_begin, key_end, tid);
-  for (int tile0 = key_begin; tile0 < key_end; tile0 += kKeyTile) {
+  if (ntiles > 0) stage.load(kb, vb, tm.key0(0), tm.lim, tid);
+  for (int t_i = 0; t_i < ntiles; ++t_i) {
+    const int tile0 = tm.key0(t_i);
     __syncthreads();
     stage.store(sk, sv, tid);
     __syncthreads();
-    if (tile0 + kKeyTile < key_end) stage.load(kb, vb, tile0 + kKeyTile, key_end, tid);
+    if (t_i + 1 < ntiles) stage.load(kb, vb, tm.key0(t_i + 1), tm.lim, tid);
     if (!wave_live) continue;
     f32x16 s[2];
 #pragma unroll
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
       for (int t = 0; t < D / 2; ++t)
         s[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sk[key * (D + 1) + 2 * t + hl], qf[t], s[c], 0, 0, 0);
     }
-    softmax_tile<kDt, 2>(s, o, m, lsum, tile0, key_end, hl, p.scale_log2);
+    softmax_tile<kDt, 2>(s, o, m, lsum, tile0, tm.lim, hl, p.scale_log2);
     // k-step u takes key 32c + 8(j/4) + 4hl + j%4 (c = u/16, j = u%16) from both operands
 #pragma unroll
     for (int u = 0; u < 32; ++u) {

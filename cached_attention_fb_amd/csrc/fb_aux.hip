@@ -18,7 +18,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 // splits are folded in a fixed order, 16 at a time with all their loads in
 // flight, keeping a running max (an online form of the same sum).  Under
 // gamma it writes the other slot and sums <A_new, A_old>, |A_new|^2, |A_old|^2
-// over its rows for the similarity.
+// over its rows for the similarity.  In total mode (sparse attention: the
+// splits are the kept keys) the fold starts from the head's cached part and
+// the result goes to the total buffer.
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p) {
   constexpr int kLpr = D / 4;
@@ -44,6 +46,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     const float* ap = p.part_o + grow * D + 4 * c4;
     float mx = -INFINITY, wsum = 0.0f;
     f32x4 acc = {0, 0, 0, 0};
+    const bool tot = p.tot_o != nullptr;
+    if (tot && p.valid[bh] != 0) {   // the cached part enters as one more term, normalised (weight 1 at its max)
+      const float l0 = p.slot_l[src * p.slot_l_stride + grow];
+      if (l0 > -INFINITY) {
+        mx = l0;
+        wsum = 1.0f;
+        acc = *reinterpret_cast<const f32x4*>(p.slot_o + src * p.slot_o_stride + grow * D + 4 * c4);
+      }
+    }
     int s = 0;
     constexpr int kBatch = 16;   // splits whose loads are in flight together
     for (; s + kBatch <= splits; s += kBatch) {
@@ -95,8 +106,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
         no += a_old[e] * a_old[e];
       }
     }
-    *reinterpret_cast<f32x4*>(p.slot_o + dst * p.slot_o_stride + grow * D + 4 * c4) = a_new;
-    if (c4 == 0) p.slot_l[dst * p.slot_l_stride + grow] = lse;
+    float* od = tot ? p.tot_o + grow * D : p.slot_o + dst * p.slot_o_stride + grow * D;
+    float* ld = tot ? p.tot_l + grow : p.slot_l + dst * p.slot_l_stride + grow;
+    *reinterpret_cast<f32x4*>(od + 4 * c4) = a_new;
+    if (c4 == 0) *ld = lse;
   }
   if (sim_terms) {
     dot = wave_sum(dot);
@@ -109,7 +122,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
       t[2] = no;
     }
   }
-  if (!p.to_other_slot && ch == 0 && tid == 0) p.valid[bh] = 1;
+  if (!p.to_other_slot && p.tot_o == nullptr && ch == 0 && tid == 0) p.valid[bh] = 1;
 }
 
 // Gamma decisions, one workgroup per head: similarity of a recomputed head
@@ -175,7 +188,54 @@ __global__ __launch_bounds__(kThreads) void reset_kernel(const ResetParams p) {
   if (p.cum != nullptr && bh < p.batch) p.cum[bh] = 0;
 }
 
+// Tile list of the prefix keys a sparse selection leaves out, one workgroup
+// per (sequence, kv head): the selected tiles are marked in an LDS bitmap,
+// then the unmarked tiles of [0, tiles) are written in ascending order (a
+// workgroup-wide prefix count per 256 tiles) and the list is padded with -1
+// (no key) to `stride` entries.  Entries of sel outside [0, tiles) mark
+// nothing.
+__global__ __launch_bounds__(kThreads) void complement_kernel(const ComplementParams p) {
+  extern __shared__ uint32_t bits[];
+  __shared__ int wave_cnt[kThreads / 64];
+  const int grp = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int words = (p.tiles + 31) / 32;
+  for (int i = tid; i < words; i += kThreads) bits[i] = 0u;
+  __syncthreads();
+  const int32_t* sel = p.sel + (int64_t)grp * p.n_sel;
+  for (int i = tid; i < p.n_sel; i += kThreads) {
+    const int t = sel[i];
+    if (t >= 0 && t < p.tiles) atomicOr(&bits[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  int32_t* out = p.comp + (int64_t)grp * p.stride;
+  int base = 0;
+  for (int t0 = 0; t0 < p.tiles; t0 += kThreads) {
+    const int t = t0 + tid;
+    const bool left = t < p.tiles && ((bits[t >> 5] >> (t & 31)) & 1u) == 0u;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(left);
+    if (lane == 0) wave_cnt[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = base, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      off += w < wave ? wave_cnt[w] : 0;
+      total += wave_cnt[w];
+    }
+    if (left) out[off + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = t;   // < tiles <= stride
+    base += total;
+    __syncthreads();   // wave_cnt is rewritten next round
+  }
+  for (int i = base + tid; i < p.stride; i += kThreads) out[i] = -1;
+}
+
 }  // namespace
+
+hipError_t launch_complement(const ComplementParams& p, hipStream_t s) {
+  if (p.groups == 0) return hipSuccess;
+  const size_t lds = (size_t)((p.tiles + 31) / 32) * 4;
+  hipLaunchKernelGGL(complement_kernel, dim3(p.groups), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, hipStream_t s) {
   return dtype == FB_BF16 ? launch_attn_bf16(head_dim, mode, p, s) : launch_attn_f32(head_dim, mode, p, s);

@@ -152,6 +152,50 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
   return it;
 }
 
+// Key tiles of a work item.  Contiguous range: tile v starts at key
+// key_begin + 64v and keys at or past key_end (the range's end) hold no key.
+// Tile list: tile v starts at key 64 * list[v] (the item's part of its group's
+// list); keys at or past n_phys hold no key, and an entry outside the
+// prefix's tiles maps to a tile with none (its loads stay in bounds).
+struct TileMap {
+  const int32_t* list;
+  int key_begin;
+  int lim;          // first key that holds no key
+  int phys_tiles;
+  __device__ __forceinline__ int key0(int v) const {
+    if (list == nullptr) return key_begin + v * kKeyTile;
+    const int t = load_scalar(list + v);
+    return (t >= 0 && t < phys_tiles) ? t * kKeyTile : lim;
+  }
+  // A wave-uniform list entry through the scalar data path: a vector load
+  // here would make the compiler wait for every vector memory operation in
+  // flight (the K/V ring's DMA loads included) before the entry is used.
+  // The list is written by an earlier launch, so the scalar cache holds no
+  // stale copy.
+  __device__ __forceinline__ static int load_scalar(const int32_t* ptr) {
+    const uint64_t a = (uint64_t)(uintptr_t)ptr;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const auto cp = (const __attribute__((address_space(4))) int32_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return *cp;
+  }
+};
+__device__ __forceinline__ TileMap tile_map(const AttnParams& p, int b, int g, int key_begin, int key_end) {
+  TileMap m;
+  if (p.tiles == nullptr) {
+    m.list = nullptr;
+    m.key_begin = key_begin;
+    m.lim = key_end;
+    m.phys_tiles = 0;
+  } else {
+    m.list = p.tiles + ((int64_t)b * p.hkv + g) * p.tiles_stride + key_begin / kKeyTile;
+    m.key_begin = 0;
+    m.lim = p.n_phys;
+    m.phys_tiles = (p.n_phys + kKeyTile - 1) / kKeyTile;
+  }
+  return m;
+}
+
 // Online-softmax update of NH 32-key halves of S^T (raw scores) whose first
 // key is key0.  c = softmax scale * log2(e) > 0, so the max of the raw scores
 // gives the max of the scaled ones and P = exp2(c*s - m) takes one FMA per

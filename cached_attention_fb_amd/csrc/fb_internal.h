@@ -52,7 +52,14 @@ struct AttnParams {
   const void* k;          // [B][Hkv][kv_cap][D]
   const void* v;
   int64_t kv_cap;         // rows per (b, kv head) in k/v
-  int32_t n_keys;         // keys 0..n_keys-1 are attended
+  int32_t n_keys;         // keys 0..n_keys-1 are attended (tile list: 64 per listed tile)
+  // Tile list (partial mode) or null.  Key tile v of group (b, g) is then the
+  // 64 prefix rows starting at 64 * tiles[(b*hkv + g)*tiles_stride + v]; rows
+  // at or past n_phys, and whole entries outside [0, ceil(n_phys/64)), hold
+  // no key.
+  const int32_t* tiles;
+  int32_t tiles_stride;
+  int32_t n_phys;
   int32_t batch, hq, hkv, bs, rows;   // rows = (Hq/Hkv) * Bs
   int32_t waves;          // wave64 per workgroup
   int32_t ksplit;         // 1, or 2: two wave sets split every key tile (waves/ksplit own 32 rows each)
@@ -97,6 +104,21 @@ struct CombineParams {
   uint8_t* valid;
   int32_t to_other_slot;  // 1: write slot cur^1 and sum similarity terms (gamma)
   float* cos_part;        // [B*Hq][row_chunks][3]
+  // Total mode (tot_o not null): the fold starts from the head's cached part
+  // (slot cur, when valid) and the result goes to tot_o [B][Hq][Bs][D] /
+  // tot_l [B][Hq][Bs]; the cache and its flags are left as they are.
+  float* tot_o;
+  float* tot_l;
+};
+
+// Tile list of the prefix keys a sparse selection leaves out.
+struct ComplementParams {
+  const int32_t* sel;     // [groups][n_sel]
+  int32_t n_sel;
+  int32_t tiles;          // prefix tiles: ceil(prefix_len / 64)
+  int32_t* comp;          // [groups][stride]
+  int32_t stride;         // >= tiles
+  int32_t groups;
 };
 
 struct DecideParams {
@@ -129,5 +151,6 @@ hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, h
 hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s);
 hipError_t launch_decide(const DecideParams& p, hipStream_t s);
 hipError_t launch_reset(const ResetParams& p, hipStream_t s);
+hipError_t launch_complement(const ComplementParams& p, hipStream_t s);
 
 }  // namespace fbk

@@ -90,11 +90,16 @@ struct fb_cache {
   float* part_l = nullptr;   // [splits_cap][B][Hq][Bs]
   float* cos_part = nullptr; // [B][Hq][row_chunks][3]
   int32_t* cum = nullptr;    // [B] cumulative rule decided on the device: updated tokens since b's last computation
+  float* tot_o = nullptr;    // [B][Hq][Bs][D] sparse steps: cached part merged with the kept keys' part
+  float* tot_l = nullptr;    // [B][Hq][Bs]
+  int32_t* comp = nullptr;   // [B*Hkv][comp_stride] sparse steps: prefix tiles the selection leaves out
+  int comp_stride = 1;       // ceil(max_prefix / 64), at least 1
   // host state
   int64_t steps = 0;         // fb_step calls since the last reset
   int32_t block_prefix = -1; // prefix_len of the current block
   int32_t block_policy = -1;
   int32_t block_dev_m = -1;  // 1: the block's threshold decisions are made on the device
+  int32_t block_n_sel = -1;  // sparse blocks: kept tiles per group; -1: a dense block
   std::vector<uint8_t> host_valid;   // [B]: every head of b holds a computed A_out (tau bookkeeping)
   std::vector<int64_t> cum_updated;  // [B]: TAU_CUM, updated tokens summed since b's last computation
   // profiling
@@ -236,17 +241,33 @@ fbk::AttnParams attn_common(const fb_cache* c, const void* q, int waves, int ksp
   return p;
 }
 
-// External attention over prefix rows 0..n-1 for the heads `sel` selects, and
-// the split combine into the cache.  rec != null: the attention launch records
+// Prefix keys of an external launch: rows 0..n_keys-1, or (tiles not null)
+// the listed 64-row tiles of each group, n_keys = 64 per listed tile.
+struct KeySet {
+  int32_t n_keys;
+  const int32_t* tiles;
+  int32_t stride;
+  int32_t n_phys;
+};
+KeySet dense_keys(int32_t n) { return KeySet{n, nullptr, 0, n}; }
+
+// External attention over a key set for the heads `sel` selects, and the
+// split combine into the cache.  rec != null: the attention launch records
 // its per-head decisions there and the combine selects from that record.
-fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* vp, int32_t n,
+// to_total: the combine adds the head's cached part and writes the total
+// buffer instead (the cache is not touched).
+fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* vp, const KeySet& ks,
                        const fbk::HeadSel& sel, int active_groups, bool gamma, hipStream_t s,
-                       uint8_t* rec = nullptr) {
+                       uint8_t* rec = nullptr, bool to_total = false) {
+  const int32_t n = ks.n_keys;
   fbk::AttnParams p = attn_common(c, q, c->ext_waves, c->ext_ksplit);
   p.k = kp;
   p.v = vp;
   p.kv_cap = c->cfg.max_prefix;
   p.n_keys = n;
+  p.tiles = ks.tiles;
+  p.tiles_stride = ks.stride;
+  p.n_phys = ks.n_phys;
   p.splits = choose_splits(c, n, active_groups);
   const int tiles = (n + fbk::kKeyTile - 1) / fbk::kKeyTile;
   p.keys_per_split = std::max(1, (tiles + p.splits - 1) / p.splits) * fbk::kKeyTile;
@@ -270,17 +291,21 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   p.part_o_stride = elems_per_slot(c->cfg);
   p.part_l_stride = rows_per_slot(c->cfg);
   ProfRec r;
-  prof_begin(c, s, &r, 0);
-  hipError_t e = fbk::launch_attn(c->cfg.dtype, c->cfg.head_dim, fbk::kModePartial, p, s);
-  prof_end(c, s, &r);
-  if (e != hipSuccess) return hip_fail(e, "external attention launch");
+  hipError_t e = hipSuccess;
+  const bool skip_attn = to_total && n == 0;   // nothing kept: the total is the cached part
+  if (!skip_attn) {
+    prof_begin(c, s, &r, to_total ? 5 : 0);
+    e = fbk::launch_attn(c->cfg.dtype, c->cfg.head_dim, fbk::kModePartial, p, s);
+    prof_end(c, s, &r);
+    if (e != hipSuccess) return hip_fail(e, "external attention launch");
+  }
 
   fbk::CombineParams cp{};
   cp.part_o = c->part_o;
   cp.part_l = c->part_l;
   cp.part_o_stride = p.part_o_stride;
   cp.part_l_stride = p.part_l_stride;
-  cp.splits = p.splits;
+  cp.splits = skip_attn ? 0 : p.splits;
   cp.batch = c->cfg.batch;
   cp.hq = c->cfg.n_q_heads;
   cp.hkv = c->cfg.n_kv_heads;
@@ -301,7 +326,11 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   cp.valid = c->valid;
   cp.to_other_slot = gamma ? 1 : 0;
   cp.cos_part = c->cos_part;
-  prof_begin(c, s, &r, 1);
+  if (to_total) {
+    cp.tot_o = c->tot_o;
+    cp.tot_l = c->tot_l;
+  }
+  prof_begin(c, s, &r, to_total ? 6 : 1);
   e = fbk::launch_combine(c->cfg.head_dim, cp, s);
   prof_end(c, s, &r);
   if (e != hipSuccess) return hip_fail(e, "split combine launch");
@@ -310,7 +339,7 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
 
 fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* vb, void* out,
                        const fbk::HeadSel& rec_sel, uint8_t* reuse_rec, hipStream_t s,
-                       const int32_t* cum_m = nullptr) {
+                       const int32_t* cum_m = nullptr, bool from_total = false) {
   fbk::AttnParams p = attn_common(c, q, c->int_waves, c->int_ksplit);
   p.k = kb;
   p.v = vb;
@@ -323,6 +352,12 @@ fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* v
   p.slot_l = c->slot_l;
   p.slot_o_stride = elems_per_slot(c->cfg);
   p.slot_l_stride = rows_per_slot(c->cfg);
+  if (from_total) {   // the external part is the total buffer (every head holds one)
+    p.slot_o = c->tot_o;
+    p.slot_l = c->tot_l;
+    p.slot_o_stride = 0;
+    p.slot_l_stride = 0;
+  }
   p.cur = c->cur;
   p.valid = c->valid;
   p.out = out;
@@ -357,13 +392,15 @@ fb_status run_reset(fb_cache* c, hipStream_t s) {
   c->block_prefix = -1;
   c->block_policy = -1;
   c->block_dev_m = -1;
+  c->block_n_sel = -1;
   std::fill(c->host_valid.begin(), c->host_valid.end(), 0);
   std::fill(c->cum_updated.begin(), c->cum_updated.end(), 0);
   return FB_OK;
 }
 
 void free_all(fb_cache* c) {
-  void* ptrs[] = {c->slot_o, c->slot_l, c->cur, c->valid, c->reuse, c->sim, c->part_o, c->part_l, c->cos_part, c->cum};
+  void* ptrs[] = {c->slot_o, c->slot_l, c->cur,   c->valid, c->reuse, c->sim,  c->part_o,
+                  c->part_l, c->cos_part, c->cum, c->tot_o, c->tot_l, c->comp};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& r : c->prof_recs) {
@@ -430,6 +467,7 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
   }
   if (cfg->kv_splits > 0) c->splits_cap = std::max(c->splits_cap, std::min(cfg->kv_splits, fbk::kMaxSplits));
 
+  c->comp_stride = std::max(1, (cfg->max_prefix + fbk::kKeyTile - 1) / fbk::kKeyTile);
   const int64_t nh = (int64_t)cfg->batch * cfg->n_q_heads;
   const size_t so = elems_per_slot(*cfg) * sizeof(float), sl = rows_per_slot(*cfg) * sizeof(float);
   struct {
@@ -446,6 +484,9 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
       {(void**)&c->part_l, (size_t)c->splits_cap * sl},
       {(void**)&c->cos_part, (size_t)nh * c->row_chunks * 3 * sizeof(float)},
       {(void**)&c->cum, (size_t)cfg->batch * sizeof(int32_t)},
+      {(void**)&c->tot_o, so},
+      {(void**)&c->tot_l, sl},
+      {(void**)&c->comp, (size_t)cfg->batch * cfg->n_kv_heads * c->comp_stride * sizeof(int32_t)},
   };
   for (auto& a : plan) {
     e = hipMalloc(a.p, std::max<size_t>(a.n, 256));
@@ -501,7 +542,7 @@ fb_status fb_external_attn(fb_cache* c, const void* q_blk, const void* k_prefix,
   fbk::HeadSel sel = all_heads(c);
   sel.flags = head_mask;
   sel.flags_select = 1;
-  fb_status st = run_external(c, q_blk, k_prefix, v_prefix, prefix_len, sel,
+  fb_status st = run_external(c, q_blk, k_prefix, v_prefix, dense_keys(prefix_len), sel,
                               c->cfg.batch * c->cfg.n_kv_heads, false, (hipStream_t)stream);
   if (st != FB_OK) return st;
   std::fill(c->host_valid.begin(), c->host_valid.end(), head_mask ? 0 : 1);
@@ -518,9 +559,24 @@ fb_status fb_internal_attn_merge(fb_cache* c, const void* q_blk, const void* k_b
   return st == FB_OK ? ok() : st;
 }
 
-fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, const void* k_blk,
-                  const void* v_blk, const void* k_prefix, const void* v_prefix, int32_t prefix_len,
-                  void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Sparse attention's kept prefix tiles for a step (null: a dense step).
+struct SparseSel {
+  const int32_t* sel;   // device int32 [B][Hkv][n_sel]
+  int32_t n_sel;
+};
+
+// One denoising step, dense or over a sparse selection.  Dense: the cached
+// external part covers prefix rows 0..prefix_len-1.  Sparse: it covers the
+// prefix tiles the selection leaves out (their list is built at the block's
+// first step), and the kept tiles are attended afresh for every head at every
+// step and folded with it into the total buffer that the merge reads.
+fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, const void* k_blk,
+                    const void* v_blk, const void* k_prefix, const void* v_prefix, int32_t prefix_len,
+                    const SparseSel* sp, void* out, void* stream) {
   if (!c) return fail(FB_E_ARG, "cache is null");
   if (!pa) return fail(FB_E_ARG, "policy args are null");
   if (!q_blk || !k_blk || !v_blk || !out) return fail(FB_E_ARG, "a tensor pointer is null");
@@ -537,10 +593,16 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
                 prefix_len, c->block_prefix);
   if (c->steps > 0 && pa->policy != c->block_policy)
     return fail(FB_E_STATE, "policy changed inside a block (reset first)");
+  const int32_t n_tiles = (prefix_len + fbk::kKeyTile - 1) / fbk::kKeyTile;
+  if (sp) {
+    if (sp->n_sel < 0 || sp->n_sel > n_tiles)
+      return fail(FB_E_SHAPE, "n_sel %d outside [0, %d prefix tiles]", sp->n_sel, n_tiles);
+    if (sp->n_sel > 0 && !sp->sel) return fail(FB_E_ARG, "sel is null");
+  }
+  const int32_t n_sel = sp ? sp->n_sel : -1;
+  if (c->steps > 0 && n_sel != c->block_n_sel)
+    return fail(FB_E_STATE, "the sparse selection (or its absence) changed inside a block (reset first)");
   const int B = c->cfg.batch;
-  // sequences whose heads recompute the external part (TAU decides per sequence)
-  fbk::HeadSel sel{};
-  int active = 0;
   const bool dev_m = tau_like && pa->n_updated_dev != nullptr;
   if (tau_like) {
     if (pa->tau < 0) return fail(FB_E_ARG, "tau %d is negative", pa->tau);
@@ -553,6 +615,9 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   if (c->steps > 0 && (dev_m ? 1 : 0) != c->block_dev_m)
     return fail(FB_E_STATE, "decisions moved between host and device inside a block (reset first)");
   if (gamma_like && !(pa->gamma == pa->gamma)) return fail(FB_E_ARG, "gamma is NaN");
+  // sequences whose heads recompute the external part (TAU decides per sequence)
+  fbk::HeadSel sel{};
+  int active = 0;
   std::vector<uint8_t> reuse_seq(B, 0);
   for (int b = 0; b < B && !dev_m; ++b) {
     bool reuse = false;
@@ -571,13 +636,35 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
   const int64_t nh = (int64_t)B * c->cfg.n_q_heads;
   uint8_t* reuse_now = c->reuse + (c->steps & 1) * nh;
   uint8_t* reuse_next = c->reuse + ((c->steps + 1) & 1) * nh;
+  // the cached external part: the whole prefix, or the tiles the selection leaves out
+  KeySet cached = dense_keys(prefix_len);
+  if (sp) {
+    cached = KeySet{(n_tiles - n_sel) * fbk::kKeyTile, c->comp, c->comp_stride, prefix_len};
+    if (c->steps == 0) {
+      fbk::ComplementParams cpl{};
+      cpl.sel = sp->sel;
+      cpl.n_sel = n_sel;
+      cpl.tiles = n_tiles;
+      cpl.comp = c->comp;
+      cpl.stride = c->comp_stride;
+      cpl.groups = B * c->cfg.n_kv_heads;
+      ProfRec r;
+      prof_begin(c, s, &r, 7);
+      hipError_t e = fbk::launch_complement(cpl, s);
+      prof_end(c, s, &r);
+      if (e != hipSuccess) return hip_fail(e, "complement launch");
+    }
+  }
 
   fb_status st = FB_OK;
+  fbk::HeadSel rec_sel = sel;     // what the merge launch records or follows
+  uint8_t* rec = nullptr;         // decisions the merge launch records (host threshold)
+  const int32_t* cum_m = nullptr;
   if (gamma_like) {
     sel = all_heads(c);
     sel.flags = reuse_now;
     sel.flags_select = 0;   // compute the heads not marked for reuse
-    st = run_external(c, q_blk, k_prefix, v_prefix, prefix_len, sel, B * c->cfg.n_kv_heads, true, s);
+    st = run_external(c, q_blk, k_prefix, v_prefix, cached, sel, B * c->cfg.n_kv_heads, true, s);
     if (st != FB_OK) return st;
     fbk::DecideParams dp{};
     dp.n_heads = (int32_t)nh;
@@ -596,7 +683,7 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
     hipError_t e = fbk::launch_decide(dp, s);
     prof_end(c, s, &r);
     if (e != hipSuccess) return hip_fail(e, "decision launch");
-    st = run_internal(c, q_blk, k_blk, v_blk, out, sel, nullptr, s);
+    rec_sel = sel;
   } else if (dev_m) {
     // threshold decided in the external launch from the counts in device
     // memory; it records the decisions, the later launches follow them
@@ -605,35 +692,60 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, cons
     sel.tau = pa->tau;
     sel.valid = c->valid;
     sel.cum = pa->policy == FB_POLICY_TAU_CUM ? c->cum : nullptr;
-    st = run_external(c, q_blk, k_prefix, v_prefix, prefix_len, sel, B * c->cfg.n_kv_heads, false, s, reuse_now);
+    st = run_external(c, q_blk, k_prefix, v_prefix, cached, sel, B * c->cfg.n_kv_heads, false, s, reuse_now);
     if (st != FB_OK) return st;
-    fbk::HeadSel rec = all_heads(c);
-    rec.flags = reuse_now;
-    rec.flags_select = 0;
-    st = run_internal(c, q_blk, k_blk, v_blk, out, rec, nullptr, s,
-                      pa->policy == FB_POLICY_TAU_CUM ? pa->n_updated_dev : nullptr);
+    rec_sel = all_heads(c);
+    rec_sel.flags = reuse_now;
+    rec_sel.flags_select = 0;
+    if (pa->policy == FB_POLICY_TAU_CUM) cum_m = pa->n_updated_dev;
   } else {
     sel.flags = nullptr;
     sel.flags_select = 1;
     if (active > 0) {
-      st = run_external(c, q_blk, k_prefix, v_prefix, prefix_len, sel, active * c->cfg.n_kv_heads, false, s);
+      st = run_external(c, q_blk, k_prefix, v_prefix, cached, sel, active * c->cfg.n_kv_heads, false, s);
       if (st != FB_OK) return st;
     }
-    st = run_internal(c, q_blk, k_blk, v_blk, out, sel, reuse_now, s);
-    if (st == FB_OK) {
-      std::fill(c->host_valid.begin(), c->host_valid.end(), 1);
-      for (int b = 0; b < B; ++b)   // TAU_CUM: the sum restarts where a sequence recomputed
-        c->cum_updated[b] = reuse_seq[b] ? c->cum_updated[b] + pa->n_updated[b] : 0;
-    }
+    rec_sel = sel;
+    rec = reuse_now;
   }
+  if (sp) {   // the kept tiles, afresh for every head, folded with the cached part
+    const KeySet kept{n_sel * fbk::kKeyTile, sp->sel, n_sel, prefix_len};
+    st = run_external(c, q_blk, k_prefix, v_prefix, kept, all_heads(c), B * c->cfg.n_kv_heads, false, s,
+                      nullptr, true);
+    if (st != FB_OK) return st;
+  }
+  st = run_internal(c, q_blk, k_blk, v_blk, out, rec_sel, rec, s, cum_m, sp != nullptr);
   if (st != FB_OK) return st;
+  if (!gamma_like && !dev_m) {
+    std::fill(c->host_valid.begin(), c->host_valid.end(), 1);
+    for (int b = 0; b < B; ++b)   // TAU_CUM: the sum restarts where a sequence recomputed
+      c->cum_updated[b] = reuse_seq[b] ? c->cum_updated[b] + pa->n_updated[b] : 0;
+  }
   if (c->steps == 0) {
     c->block_prefix = prefix_len;
     c->block_policy = pa->policy;
     c->block_dev_m = dev_m ? 1 : 0;
+    c->block_n_sel = n_sel;
   }
   c->steps += 1;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, const void* k_blk,
+                  const void* v_blk, const void* k_prefix, const void* v_prefix, int32_t prefix_len,
+                  void* out, void* stream) {
+  return step_impl(c, pa, q_blk, k_blk, v_blk, k_prefix, v_prefix, prefix_len, nullptr, out, stream);
+}
+
+fb_status fb_step_sparse(fb_cache* c, const fb_policy_args* pa, const void* q_blk, const void* k_blk,
+                         const void* v_blk, const void* k_prefix, const void* v_prefix, int32_t prefix_len,
+                         const int32_t* sel_tiles, int32_t n_sel, void* out, void* stream) {
+  const SparseSel sp{sel_tiles, n_sel};
+  return step_impl(c, pa, q_blk, k_blk, v_blk, k_prefix, v_prefix, prefix_len, &sp, out, stream);
 }
 
 fb_status fb_cache_read(const fb_cache* c, int32_t field, void* host_dst, size_t bytes, void* stream) {

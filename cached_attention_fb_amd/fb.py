@@ -21,13 +21,14 @@ FB_F32, FB_BF16 = 0, 1
 POLICY_ALWAYS, POLICY_TAU, POLICY_GAMMA, POLICY_TAU_CUM, POLICY_GAMMA_GROUP = 0, 1, 2, 3, 4
 FIELD_A_OUT, FIELD_L_OUT, FIELD_SIM, FIELD_REUSE, FIELD_VALID = range(5)
 PROFILE_KINDS = 8
-KIND_NAMES = ["external", "combine", "internal_merge", "decide", "reset"]
+KIND_NAMES = ["external", "combine", "internal_merge", "decide", "reset", "sparse_kept", "sparse_total",
+              "sparse_complement"]
 
 STATUS_NAMES = {0: "FB_OK", 1: "FB_E_ARG", 2: "FB_E_SHAPE", 3: "FB_E_DTYPE", 4: "FB_E_STATE",
                 5: "FB_E_NOMEM", 6: "FB_E_HIP", 7: "FB_E_UNSUPPORTED"}
 
 EXPORTED = ["fb_cache_alloc", "fb_cache_free", "fb_cache_reset", "fb_external_attn",
-            "fb_internal_attn_merge", "fb_step", "fb_cache_read", "fb_cache_info",
+            "fb_internal_attn_merge", "fb_step", "fb_step_sparse", "fb_cache_read", "fb_cache_info",
             "fb_profile_enable", "fb_profile_read", "fb_last_error"]
 
 
@@ -70,6 +71,7 @@ def load() -> ctypes.CDLL:
     lib.fb_external_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp]
     lib.fb_internal_attn_merge.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.fb_step.argtypes = [vp, ctypes.POINTER(FBPolicyArgs), vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.fb_step_sparse.argtypes = [vp, ctypes.POINTER(FBPolicyArgs), vp, vp, vp, vp, vp, i32, vp, i32, vp, vp]
     lib.fb_cache_read.argtypes = [vp, i32, vp, ctypes.c_size_t, vp]
     lib.fb_cache_info.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32)]
     lib.fb_profile_enable.argtypes = [vp, i32]
@@ -157,11 +159,14 @@ class Cache:
                                                _stream(stream)))
 
     def step(self, policy: int, q, k_blk, v_blk, k_prefix, v_prefix, prefix_len: int, out,
-             tau: int = 0, gamma: float = 0.0, n_updated=None, n_updated_dev=None, stream=None) -> None:
+             tau: int = 0, gamma: float = 0.0, n_updated=None, n_updated_dev=None, stream=None,
+             sel_tiles=None) -> None:
         """One denoising step.  Threshold counts come either from the host
         (`n_updated`, B ints) or from device memory (`n_updated_dev`, an int32
         tensor of B entries on the cache's device), in which case the
-        decisions are made on the device."""
+        decisions are made on the device.  `sel_tiles` (int32 device tensor
+        [B, Hkv, n_sel]): a sparse attention's kept prefix tiles
+        (fb_step_sparse)."""
         args = FBPolicyArgs(policy, tau, gamma, None, None)
         keep = None
         if n_updated_dev is not None:
@@ -175,17 +180,33 @@ class Cache:
             if keep.size != self.cfg.batch:
                 raise ValueError(f"n_updated needs {self.cfg.batch} entries")
             args.n_updated = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        if sel_tiles is not None:
+            sel_ptr, n_sel = self._sel(sel_tiles)
+            _check(self.lib.fb_step_sparse(self.h, ctypes.byref(args), self._q(q), self._kv_blk(k_blk, "k_blk"),
+                                           self._kv_blk(v_blk, "v_blk"), self._kv_pre(k_prefix, "k_prefix"),
+                                           self._kv_pre(v_prefix, "v_prefix"), int(prefix_len), sel_ptr, n_sel,
+                                           self._q(out, "out"), _stream(stream)))
+            return
         _check(self.lib.fb_step(self.h, ctypes.byref(args), self._q(q), self._kv_blk(k_blk, "k_blk"),
                                 self._kv_blk(v_blk, "v_blk"), self._kv_pre(k_prefix, "k_prefix"),
                                 self._kv_pre(v_prefix, "v_prefix"), int(prefix_len), self._q(out, "out"),
                                 _stream(stream)))
 
-    def prepare(self, q, k_blk, v_blk, k_prefix, v_prefix, out) -> "PreparedStep":
+    def _sel(self, t: torch.Tensor):
+        c = self.cfg
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_cuda or t.dim() != 3
+                or tuple(t.shape[:2]) != (c.batch, c.n_kv_heads) or not t.is_contiguous()):
+            raise ValueError(f"sel_tiles must be a contiguous int32 device tensor [{c.batch}, {c.n_kv_heads}, n_sel]")
+        return (t.data_ptr() if t.numel() else None), int(t.shape[2])
+
+    def prepare(self, q, k_blk, v_blk, k_prefix, v_prefix, out, sel_tiles=None) -> "PreparedStep":
         """Check a set of step buffers once; the returned object calls fb_step
-        on them with only scalar marshalling (for loops over many steps)."""
+        (fb_step_sparse with sel_tiles) on them with only scalar marshalling
+        (for loops over many steps)."""
+        sel = self._sel(sel_tiles) if sel_tiles is not None else None
         return PreparedStep(self, self._q(q), self._kv_blk(k_blk, "k_blk"), self._kv_blk(v_blk, "v_blk"),
                             self._kv_pre(k_prefix, "k_prefix"), self._kv_pre(v_prefix, "v_prefix"),
-                            self._q(out, "out"), (q, k_blk, v_blk, k_prefix, v_prefix, out))
+                            self._q(out, "out"), (q, k_blk, v_blk, k_prefix, v_prefix, out, sel_tiles), sel)
 
     def read(self, field: int, stream=None) -> np.ndarray:
         c = self.cfg
@@ -227,8 +248,9 @@ class PreparedStep:
     """fb_step on buffers checked once by Cache.prepare (they are kept alive
     here).  n_updated is copied into a preallocated int32 array per call."""
 
-    def __init__(self, cache: Cache, q, kb, vb, kp, vp, out, keep):
+    def __init__(self, cache: Cache, q, kb, vb, kp, vp, out, keep, sel=None):
         self.cache, self.keep = cache, keep
+        self.sel = sel
         self.ptrs = (q, kb, vb, kp, vp)
         self.out = out
         self.m = (ctypes.c_int32 * cache.cfg.batch)()
@@ -253,7 +275,11 @@ class PreparedStep:
                 for i, v in enumerate(n_updated):
                     self.m[i] = int(v)
         q, kb, vb, kp, vp = self.ptrs
-        code = self.fn(self.cache.h, self.args_ref, q, kb, vb, kp, vp, prefix_len, self.out,
-                       _stream(stream) if stream is None or not isinstance(stream, int) else stream)
+        st = _stream(stream) if stream is None or not isinstance(stream, int) else stream
+        if self.sel is not None:
+            code = self.cache.lib.fb_step_sparse(self.cache.h, self.args_ref, q, kb, vb, kp, vp, prefix_len,
+                                                 self.sel[0], self.sel[1], self.out, st)
+        else:
+            code = self.fn(self.cache.h, self.args_ref, q, kb, vb, kp, vp, prefix_len, self.out, st)
         if code != FB_OK:
             _check(code)

@@ -182,6 +182,35 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* p, const void* q_blk, const
                   const void* v_blk, const void* k_prefix, const void* v_prefix,
                   int32_t prefix_len, void* out, void* stream);
 
+/* One denoising step over a sparse attention (page §2, compatibility with
+ * sparse attention; §3, synergy with sparsity): a sparse selection keeps some
+ * 64-key tiles of the prefix; the tiles it leaves out are treated as the
+ * block-external set, whose part (A, L) is cached and reused under the
+ * policy exactly as fb_step does for the whole prefix, while the kept tiles
+ * are attended afresh for every head at every step.  The output is the
+ * log-space merge of the cached part, the kept part and the block-internal
+ * part.  With every head recomputing (ALWAYS) it is exact attention over the
+ * prefix and the block, whatever the selection.
+ *   sel_tiles  device int32 [B][Hkv][n_sel]: for each (sequence, kv head), the
+ *              kept tiles (tile t = prefix rows 64t .. 64t+63, cut at
+ *              prefix_len), distinct, ascending by convention; shared by the
+ *              query heads of the kv head.  Entries outside [0, ceil(prefix_len
+ *              / 64)) keep nothing.  Read at the block's first step (which
+ *              lists the tiles left out) and at every step (kept tiles): the
+ *              selection must stay the same within a block.
+ *   n_sel      0 <= n_sel <= ceil(prefix_len / 64), the same for every step of
+ *              a block.
+ * Under GAMMA the similarity is that of the cached (left-out) part.  The
+ * cache fields A_out/L_out hold the left-out keys' part.  Policies, counts,
+ * graph capture and asynchrony are as for fb_step; a block is either dense
+ * (fb_step) or sparse (fb_step_sparse) until its reset.  Errors: those of
+ * fb_step, FB_E_ARG (sel_tiles null with n_sel > 0), FB_E_SHAPE (n_sel out of
+ * range), FB_E_STATE (n_sel, or sparse vs dense, changed inside a block). */
+fb_status fb_step_sparse(fb_cache* c, const fb_policy_args* p, const void* q_blk, const void* k_blk,
+                         const void* v_blk, const void* k_prefix, const void* v_prefix,
+                         int32_t prefix_len, const int32_t* sel_tiles, int32_t n_sel, void* out,
+                         void* stream);
+
 /* Copy one field of the cache (layouts in the FB_FIELD_* list) to host
  * memory `host_dst` of exactly `bytes` bytes, after the work already on
  * `stream`.  Synchronising; meant for tests and debugging.
@@ -198,7 +227,9 @@ fb_status fb_cache_info(const fb_cache* c, size_t* device_bytes, int32_t* kv_spl
  * and returns, per kernel kind, the number of launches and their summed
  * duration in milliseconds since enabling (and clears the record).  Kinds:
  * 0 external attention, 1 split combine, 2 internal attention + merge,
- * 3 similarity / decision, 4 reset.  At most FB_PROFILE_KINDS kinds. */
+ * 3 similarity / decision, 4 reset, 5 sparse kept-tile attention, 6 sparse
+ * total combine, 7 sparse left-out tile list.  At most FB_PROFILE_KINDS
+ * kinds. */
 #define FB_PROFILE_KINDS 8
 typedef struct {
   int64_t launches[FB_PROFILE_KINDS];

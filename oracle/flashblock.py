@@ -251,7 +251,11 @@ SPARSE_TILE = 64   # prefix keys per selectable tile (the selection's granularit
 def tile_rows(tiles: Sequence[int], n_prefix: int, tile: int = SPARSE_TILE) -> np.ndarray:
     """Prefix rows of the listed key tiles (tile t holds rows tile*t ..
     tile*t + tile - 1, cut at n_prefix), ascending."""
-    rows = [np.arange(t * tile, min((t + 1) * tile, n_prefix)) for t in sorted(set(int(t) for t in tiles))]
+    tiles = [int(t) for t in tiles]
+    n_tiles = (n_prefix + tile - 1) // tile
+    if len(set(tiles)) != len(tiles) or any(t < 0 or t >= n_tiles for t in tiles):
+        raise ValueError("a selection lists distinct tiles of the prefix")
+    rows = [np.arange(t * tile, min((t + 1) * tile, n_prefix)) for t in sorted(tiles)]
     return np.concatenate(rows).astype(np.int64) if rows else np.zeros(0, np.int64)
 
 
