@@ -301,6 +301,103 @@ def graph_bench(name, blocks=8, warmup=2):
     return res
 
 
+def sparse_bench(name, densities=(0.2, 0.3, 0.4), blocks=4, warmup=1):
+    """FlashBlock over a sparse attention (fb_step_sparse): synthetic tile
+    selections at several densities, every layer its own.  Per density: µs
+    per layer-step under the workload's threshold and under always-recompute,
+    and the kept-tile attention kernel (HIP events, profiled threshold pass)
+    against the HBM roofline of its kept K/V; beside them the dense path
+    under the same threshold."""
+    import torch
+    from cached_attention_fb_amd import fb
+    from cached_attention_fb_amd import workload as wl
+
+    w = wl.workload(name)
+    inp = wl.generate(w)
+    blk = inp.blocks[0]
+    S = len(blk.steps)
+    n = w.prefix
+    kv_bytes, _, _ = algorithmic(w, n)
+    layers = max(1, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+    pol = {"tau": fb.POLICY_TAU, "tau_cum": fb.POLICY_TAU_CUM}[w.policy]
+    dev = "cuda"
+    kp0 = inp.k_prefix.to(dev)
+    vp0 = inp.v_prefix.to(dev)
+    prefixes = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(layers - 1)]
+    caches = [fb.Cache(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block, n, w.torch_dtype)
+              for _ in range(layers)]
+    qs = [st.q.to(dev) for st in blk.steps]
+    ks = [st.k.to(dev) for st in blk.steps]
+    vs = [st.v.to(dev) for st in blk.steps]
+    ms = [np.ascontiguousarray(st.n_updated, dtype=np.int32) for st in blk.steps]
+    del inp, blk
+    outs = [torch.empty_like(qs[0]) for _ in range(layers)]
+
+    def run(prepared, policy, n_blocks):
+        for _ in range(n_blocks):
+            for s in range(S):
+                for li in range(layers):
+                    if s == 0:
+                        caches[li].reset()
+                    prepared[li][s](policy, n, ms[s], w.tau, 0.0)
+
+    def timed(prepared, policy):
+        run(prepared, policy, warmup)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run(prepared, policy, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / (blocks * S * layers)
+
+    dense = [[c.prepare(qs[s], ks[s], vs[s], prefixes[li][0], prefixes[li][1], outs[li]) for s in range(S)]
+             for li, c in enumerate(caches)]
+    res = {"workload": name, "layers": layers, "policy": w.policy, "tau": w.tau,
+           "dense_tau_us_per_layer_step": round(timed(dense, pol), 3),
+           "dense_always_us_per_layer_step": round(timed(dense, fb.POLICY_ALWAYS), 3), "densities": {}}
+    del dense
+    for dens in densities:
+        sels = [torch.as_tensor(wl.sparse_selection(w, n, dens, seed=w.seed + li)).to(dev).contiguous()
+                for li in range(layers)]
+        n_sel = int(sels[0].shape[2])
+        prep = [[c.prepare(qs[s], ks[s], vs[s], prefixes[li][0], prefixes[li][1], outs[li], sel_tiles=sels[li])
+                 for s in range(S)] for li, c in enumerate(caches)]
+        tau_us = timed(prep, pol)
+        always_us = timed(prep, fb.POLICY_ALWAYS)
+        for c in caches:
+            c.profile_enable(True)
+        run(prep, pol, 1)
+        torch.cuda.synchronize()
+        prof = {}
+        for c in caches:
+            for kname, (cnt, tms) in c.profile_read().items():
+                a, b = prof.get(kname, (0, 0.0))
+                prof[kname] = (a + cnt, b + tms)
+            c.profile_enable(False)
+        kern = {k: round(1e3 * v[1] / v[0], 3) for k, v in prof.items() if v[0]}
+        kept_rows = min(n, n_sel * 64)
+        kept_kv = 2 * w.batch * w.n_kv_heads * kept_rows * w.head_dim * w.elem_bytes
+        q_b = w.batch * w.n_q_heads * w.block * w.head_dim * w.elem_bytes
+        out_b = w.batch * w.n_q_heads * w.block * (w.head_dim + 1) * 4
+        kept_roof = None
+        if "sparse_kept" in kern:
+            kept_roof = roofline(w, kern["sparse_kept"], kept_kv + q_b + out_b,
+                                 4.0 * w.batch * w.n_q_heads * w.block * kept_rows * w.head_dim)
+        res["densities"][str(dens)] = {
+            "kept_tiles": n_sel, "kept_fraction": round(n_sel * 64 / n, 4),
+            "tau_us_per_layer_step": round(tau_us, 3), "always_us_per_layer_step": round(always_us, 3),
+            "reuse_vs_full_speedup": round(always_us / tau_us, 3), "kernel_avg_us_tau": kern,
+            "kept_attention_roofline": kept_roof}
+        del prep, sels
+    for c in caches:
+        c.close()
+    del caches, prefixes, kp0, vp0, qs, ks, vs, outs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def staleness(name, policies):
     """Output error of each reuse policy against always-recompute on the same
     seeded block (one layer): max |out - out_always| / max |out_always| and the
@@ -504,6 +601,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate", action="store_true", help="only run the known-traffic reference kernel")
     ap.add_argument("--sweep", action="store_true", help="only run the multi-block long-context prefix sweep")
+    ap.add_argument("--sparse", action="store_true",
+                    help="only run FlashBlock over a sparse attention at densities 0.2/0.3/0.4")
     ap.add_argument("--graph", action="store_true",
                     help="only run device-side threshold decisions, eager and as HIP graphs")
     args = ap.parse_args()
@@ -523,6 +622,9 @@ def main():
         return
     if args.graph:
         print(json.dumps(graph_bench(args.workload)), flush=True)
+        return
+    if args.sparse:
+        print(json.dumps(sparse_bench(args.workload)), flush=True)
         return
 
     # the largest prefix one layer's K/V can take in the free device memory
@@ -593,6 +695,8 @@ def main():
         result["policy_variants"] = variants
         # threshold decisions on the device, eager and replayed as HIP graphs
         result["device_decisions"] = graph_bench(w.name if w.policy in ("tau", "tau_cum") else "dllm-8k")
+        # FlashBlock over a sparse attention (left-out tiles cached, kept tiles fresh)
+        result["sparse"] = {nm: sparse_bench(nm) for nm in ("dllm-8k", "long-32k-b4")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
     print(json.dumps(result), flush=True)
