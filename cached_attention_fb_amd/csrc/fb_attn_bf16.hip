@@ -195,7 +195,7 @@ __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, c
     const int pos = ii * 64 + lane;                 // 16-byte slot inside the tile
     const int key = pos / P::kCpr, pc = pos % P::kCpr;
     const int swz = tensor == 0 ? (key & (P::kCpr - 1)) : ((4 * key) & (P::kCpr - 4));
-    const int gk = max(0, min(tile0 + key, key_end - 1));   // rows past the end: any valid row (masked later)
+    const int gk = min(tile0 + key, key_end - 1);   // rows past the end: any valid row (masked later)
     const bf16* src = (tensor == 0 ? kb : vb) + (int64_t)gk * D + (pc ^ swz) * 8;
     __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(stage + tensor * P::kTensorBytes + ii * 1024), 16, 0, 0);
   }
@@ -251,7 +251,7 @@ __device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f3
 template <int D, int ROWW>
 constexpr int xch_bytes() { return ROWW * (16 * (D / 32) + 2) * 64 * 4; }
 
-template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT>
+template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT, bool LIST>
 __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const AttnParams p) {
   constexpr int WAVES = ROWW * KSPLIT;
   constexpr int NH = 2 / KSPLIT;   // 32-key halves of a tile per wave
@@ -265,7 +265,6 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   const int rl = lane & 31, hl = lane >> 5;
   const AttnItem it = attn_item(p, MODE == kModePartial);
   if constexpr (MODE == kModePartial) record_decisions(p);
-  else update_cum(p, it.b, it.g, it.rt);
   if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
   const int b = it.b, g = it.g, grp = p.hq / p.hkv;
   const int key_begin = it.key_begin, key_end = it.key_end;
@@ -278,9 +277,12 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   const int bh = b * p.hq + g * grp + (row_ok ? row / p.bs : 0);
 
   const bf16* qg = reinterpret_cast<const bf16*>(p.q);
-  const bf16* kb = reinterpret_cast<const bf16*>(p.k) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
-  const bf16* vb = reinterpret_cast<const bf16*>(p.v) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
-  const TileMap tm = tile_map(p, b, g, key_begin, key_end);
+  // keys of the item: the prefix (or the merge launch's block), or a fused
+  // step's block for its block-internal items
+  const int64_t kv_cap = it.internal ? p.bs : p.kv_cap;
+  const bf16* kb = reinterpret_cast<const bf16*>(it.internal ? p.kblk : p.k) + ((int64_t)b * p.hkv + g) * kv_cap * D;
+  const bf16* vb = reinterpret_cast<const bf16*>(it.internal ? p.vblk : p.v) + ((int64_t)b * p.hkv + g) * kv_cap * D;
+  const TileMap<LIST> tm = tile_map<LIST>(p, it);
   const int lim = tm.lim;
 
   // Prologue loads, none waiting on another: the merge's head flags, then Q
@@ -291,8 +293,11 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   // drain the whole ring before every MFMA that reads Q.
   ExtPart<D> ext;
   const bool ext_lane = MODE == kModeMerge && row_ok && kh == 0;
-  if (ext_lane) ext.load_state(p, bh);
-  FB_LDS char* q_lds = lds + P::q_offset(P::ring_stages(p.keys_per_split)) + rw * 32 * D * 2;
+  if (ext_lane) {
+    ext.load_state(p, bh);
+    if constexpr (PREFETCH_EXT) ext.load_data(p, grow, hl);   // in flight with Q and the tiles
+  }
+  FB_LDS char* q_lds = lds + P::q_offset(P::ring_stages(p.ring_keys)) + rw * 32 * D * 2;
   if (kh == 0 && wave_live) issue_q<D>(q_lds, qg + (grow - rl) * D, p.rows - row0, lane);
   int issued;
   if (ntiles >= 2) {
@@ -323,10 +328,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   }
   // When Q sits in ring stages 2-3, every wave must have read it before the
   // first refill writes there.
-  if (P::ring_stages(p.keys_per_split) == P::kStages) __builtin_amdgcn_s_barrier();
-  if constexpr (MODE == kModeMerge && PREFETCH_EXT) {
-    if (ext_lane) ext.load_data(p, grow, hl);   // in flight while the tiles are processed
-  }
+  if (P::ring_stages(p.ring_keys) == P::kStages) __builtin_amdgcn_s_barrier();
 
   f32x16 o[kDt];
 #pragma unroll
@@ -507,7 +509,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   }
 }
 
-template <int D, int ROWW, int KSPLIT, int MODE, bool PF>
+template <int D, int ROWW, int KSPLIT, int MODE, bool PF, bool LIST>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   using P = Pipe<D, ROWW * KSPLIT>;
   const int blocks = p.grid > 0 ? p.grid : p.batch * p.hkv * p.splits * p.row_tiles;
@@ -518,25 +520,35 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
                                     KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   // a workgroup never uses more ring stages than its key range has tiles
-  const int ring = P::ring_stages(p.keys_per_split);
+  const int ring = P::ring_stages(p.ring_keys);
   int lds = std::max(ring * P::kStageBytes, P::q_offset(ring) + kQBytes);
   if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
   lds = std::max(lds, kStageOut);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF>), dim3(blocks), dim3(64 * ROWW * KSPLIT), lds, s, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST>), dim3(blocks), dim3(64 * ROWW * KSPLIT),
+                     lds, s, p);
   return hipGetLastError();
 }
 
+template <int D, int MODE, bool PF_SMALL, bool LIST>
+hipError_t launch_shape(const AttnParams& p, hipStream_t s) {
+  if (p.waves == 8 && p.ksplit == 1) return launch_one<D, 8, 1, MODE, false, LIST>(p, s);
+  if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false, LIST>(p, s);
+  return launch_one<D, 1, 1, MODE, PF_SMALL, LIST>(p, s);
+}
+
+// Tile lists occur in partial launches only (sparse steps).
 template <int D, int MODE, bool PF_SMALL>
 hipError_t launch_mode(const AttnParams& p, hipStream_t s) {
-  if (p.waves == 8 && p.ksplit == 1) return launch_one<D, 8, 1, MODE, false>(p, s);
-  if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false>(p, s);
-  return launch_one<D, 1, 1, MODE, PF_SMALL>(p, s);
+  if constexpr (MODE == kModePartial) {
+    if (p.tiles != nullptr) return launch_shape<D, MODE, PF_SMALL, true>(p, s);
+  }
+  return launch_shape<D, MODE, PF_SMALL, false>(p, s);
 }
 
 }  // namespace

@@ -48,7 +48,6 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
   const int rl = lane & 31, hl = lane >> 5;
   const AttnItem it = attn_item(p, MODE == kModePartial);
   if constexpr (MODE == kModePartial) record_decisions(p);
-  else update_cum(p, it.b, it.g, it.rt);
   if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
   const int b = it.b, g = it.g, grp = p.hq / p.hkv;
   const int key_begin = it.key_begin, key_end = it.key_end;
@@ -59,8 +58,9 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
   const int64_t grow = (int64_t)(b * p.hq + g * grp) * p.bs + row;
 
   const float* qg = reinterpret_cast<const float*>(p.q);
-  const float* kb = reinterpret_cast<const float*>(p.k) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
-  const float* vb = reinterpret_cast<const float*>(p.v) + ((int64_t)b * p.hkv + g) * p.kv_cap * D;
+  const int64_t kv_cap = it.internal ? p.bs : p.kv_cap;
+  const float* kb = reinterpret_cast<const float*>(it.internal ? p.kblk : p.k) + ((int64_t)b * p.hkv + g) * kv_cap * D;
+  const float* vb = reinterpret_cast<const float*>(it.internal ? p.vblk : p.v) + ((int64_t)b * p.hkv + g) * kv_cap * D;
 
   // Q^T as the B operand: lane (row, hl) holds Q[row][2t + hl].
   float qf[D / 2];
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
   for (int i = 0; i < kDt; ++i) o[i] = f32x16{};
   float m = -INFINITY, lsum = 0.0f;
 
-  const TileMap tm = tile_map(p, b, g, key_begin, key_end);
+  const TileMap<true> tm = tile_map<true>(p, it);
   const int ntiles = key_end > key_begin ? (key_end - key_begin + kKeyTile - 1) / kKeyTile : 0;
   F32Tile<D> stage;
   if (ntiles > 0) stage.load(kb, vb, tm.key0(0), tm.lim, tid);

@@ -1,5 +1,7 @@
 // Split combine, gamma decision and reset kernels (gfx950), and the attention
 // dispatcher.
+#include <algorithm>
+
 #include "fb_device.h"
 
 namespace fbk {
@@ -15,28 +17,35 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Split combine (page §2's log-space rule over the prefix chunks):
 // A = sum_s e^{L_s - M} A_s / sum_s e^{L_s - M}, L = M + log sum, M = max_s L_s.
 // One wave per workgroup, D/4 lanes (one float4 column each) per row.  The
-// splits are folded in a fixed order, 16 at a time with all their loads in
-// flight, keeping a running max (an online form of the same sum).  Under
-// gamma it writes the other slot and sums <A_new, A_old>, |A_new|^2, |A_old|^2
-// over its rows for the similarity.  In total mode (sparse attention: the
+// splits are folded in a fixed order, BATCH (8, 16 or 32, from the largest
+// split count the launch can see) at a time with all their loads in flight,
+// keeping a running max (an online form of the same sum).  Under
+// gamma, before replacing each cached value it sums <A_new, A_old>, |A_new|^2
+// and |A_old|^2 over its rows for the similarity.  In total mode (sparse attention: the
 // splits are the kept keys) the fold starts from the head's cached part and
 // the result goes to the total buffer.
-template <int D>
+template <int D, int BATCH>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p) {
   constexpr int kLpr = D / 4;
   constexpr int kRows = kCombineThreads / kLpr;
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / p.row_chunks, ch = blockIdx.x % p.row_chunks;
   const int b = bh / p.hq;
-  if (!head_selected(p.sel, b, bh)) return;
-  int splits = p.splits;
-  if (p.dyn.groups > 0) {   // the external launch's device plan
+  const bool out_mode = p.out != nullptr;
+  const bool sel = head_selected(p.sel, b, bh);
+  if (p.cum != nullptr && bh % p.hq == 0 && ch == 0 && tid == 0) {   // once per sequence
+    bool any = false;
+    for (int h = 0; h < p.hq; ++h) any |= head_selected(p.sel, b, b * p.hq + h);
+    p.cum[b] = any ? 0 : p.cum[b] + p.cum_m[b];
+  }
+  if (!sel && !out_mode) return;
+  int splits = sel ? p.splits : 0;
+  if (sel && p.dyn.groups > 0) {   // the external launch's device plan
     const int n = __builtin_popcountll(active_groups(p.sel, p.dyn.groups, p.hq, p.hkv));
     splits = p.dyn.splits[n];
   }
-  const int src = p.cur[bh];
-  const int dst = p.to_other_slot ? (src ^ 1) : src;
-  const bool sim_terms = p.to_other_slot && p.valid[bh] != 0;
+  const bool sim_terms = sel && p.sim_terms && p.valid[bh] != 0;
+  const bool tot = p.tot_o != nullptr;
   const int c4 = tid % kLpr;
   const int i = ch * kRows + tid / kLpr;
   float dot = 0.0f, nn = 0.0f, no = 0.0f;
@@ -46,35 +55,42 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     const float* ap = p.part_o + grow * D + 4 * c4;
     float mx = -INFINITY, wsum = 0.0f;
     f32x4 acc = {0, 0, 0, 0};
-    const bool tot = p.tot_o != nullptr;
-    if (tot && p.valid[bh] != 0) {   // the cached part enters as one more term, normalised (weight 1 at its max)
-      const float l0 = p.slot_l[src * p.slot_l_stride + grow];
+    // the cached part enters as one more term, normalised (weight 1 at its
+    // max): in total mode, and for the output of a head that reuses it
+    if ((tot || !sel) && p.valid[bh] != 0) {
+      const float l0 = p.slot_l[grow];
       if (l0 > -INFINITY) {
         mx = l0;
         wsum = 1.0f;
-        acc = *reinterpret_cast<const f32x4*>(p.slot_o + src * p.slot_o_stride + grow * D + 4 * c4);
+        acc = *reinterpret_cast<const f32x4*>(p.slot_o + grow * D + 4 * c4);
       }
     }
-    int s = 0;
-    constexpr int kBatch = 16;   // splits whose loads are in flight together
-    for (; s + kBatch <= splits; s += kBatch) {
-      float l[kBatch];
-      f32x4 a[kBatch];
+    // BATCH splits per round, all their loads in flight; past the last split
+    // a round re-reads it and gives it no weight (L = -inf)
+    for (int s = 0; s < splits; s += BATCH) {
+      float l[BATCH];
+      f32x4 a[BATCH];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        l[u] = lp[(s + u) * p.part_l_stride];
-        a[u] = *reinterpret_cast<const f32x4*>(ap + (s + u) * p.part_o_stride);
+      for (int u = 0; u < BATCH; ++u) {
+        const int si = min(s + u, splits - 1);
+        l[u] = lp[si * p.part_l_stride];
+        a[u] = *reinterpret_cast<const f32x4*>(ap + si * p.part_o_stride);
+        if (s + u >= splits) l[u] = -INFINITY;
       }
+      // keep every load of the round ahead of the arithmetic: left to itself
+      // the scheduler trades the in-flight loads for registers and waits on
+      // a few at a time
+      __builtin_amdgcn_sched_barrier(0);
       float cm = l[0];
 #pragma unroll
-      for (int u = 1; u < kBatch; ++u) cm = fmaxf(cm, l[u]);
+      for (int u = 1; u < BATCH; ++u) cm = fmaxf(cm, l[u]);
       const float nm = fmaxf(mx, cm);
       if (nm > -INFINITY) {
         const float sc = fast_exp2((mx - nm) * kLog2e);
         acc *= sc;
         wsum *= sc;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < BATCH; ++u) {
           const float w = fast_exp2((l[u] - nm) * kLog2e);
           wsum += w;
           acc += w * a[u];
@@ -82,34 +98,43 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
         mx = nm;
       }
     }
-    for (; s < splits; ++s) {
-      const float l = lp[s * p.part_l_stride];
-      const f32x4 a = *reinterpret_cast<const f32x4*>(ap + s * p.part_o_stride);
-      const float nm = fmaxf(mx, l);
+    if (sel && !(tot && out_mode)) {   // a recomputed head's new value: into the cache (total mode: the buffer)
+      const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+      const f32x4 a_new = acc * inv;
+      const float lse = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
+      if (sim_terms) {
+        const f32x4 a_old = *reinterpret_cast<const f32x4*>(p.slot_o + grow * D + 4 * c4);   // replaced below
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dot += a_new[e] * a_old[e];
+          nn += a_new[e] * a_new[e];
+          no += a_old[e] * a_old[e];
+        }
+      }
+      float* od = (tot ? p.tot_o : p.slot_o) + grow * D;
+      float* ld = (tot ? p.tot_l : p.slot_l) + grow;
+      *reinterpret_cast<f32x4*>(od + 4 * c4) = a_new;
+      if (c4 == 0) *ld = lse;
+    }
+    if (out_mode) {   // the block-internal part (page §2 merge), then the step's output
+      const float l_in = lp[p.int_split * p.part_l_stride];
+      const f32x4 a_in = *reinterpret_cast<const f32x4*>(ap + p.int_split * p.part_o_stride);
+      const float nm = fmaxf(mx, l_in);
       if (nm > -INFINITY) {
         const float sc = fast_exp2((mx - nm) * kLog2e);
-        const float w = fast_exp2((l - nm) * kLog2e);
-        acc = acc * sc + w * a;
+        const float w = fast_exp2((l_in - nm) * kLog2e);
+        acc = acc * sc + w * a_in;
         wsum = wsum * sc + w;
-        mx = nm;
+      }
+      const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+      const f32x4 r = acc * inv;
+      if (p.out_bf16) {
+        const bf16x4 rb = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(p.out) + grow * D + 4 * c4) = rb;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + grow * D + 4 * c4) = r;
       }
     }
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    const f32x4 a_new = acc * inv;
-    const float lse = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
-    if (sim_terms) {
-      const f32x4 a_old = *reinterpret_cast<const f32x4*>(p.slot_o + src * p.slot_o_stride + grow * D + 4 * c4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dot += a_new[e] * a_old[e];
-        nn += a_new[e] * a_new[e];
-        no += a_old[e] * a_old[e];
-      }
-    }
-    float* od = tot ? p.tot_o + grow * D : p.slot_o + dst * p.slot_o_stride + grow * D;
-    float* ld = tot ? p.tot_l + grow : p.slot_l + dst * p.slot_l_stride + grow;
-    *reinterpret_cast<f32x4*>(od + 4 * c4) = a_new;
-    if (c4 == 0) *ld = lse;
   }
   if (sim_terms) {
     dot = wave_sum(dot);
@@ -122,13 +147,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
       t[2] = no;
     }
   }
-  if (!p.to_other_slot && p.tot_o == nullptr && ch == 0 && tid == 0) p.valid[bh] = 1;
+  if (sel && !p.sim_terms && !tot && ch == 0 && tid == 0) p.valid[bh] = 1;
 }
 
 // Gamma decisions, one workgroup per head: similarity of a recomputed head
 // (or of its kv group: the same terms summed over the group's heads) from the
-// combine's partial terms (summed in a fixed order), slot flip, and
-// the reuse decision of the next step (strict sim > gamma; NaN, i.e. no
+// combine's partial terms (summed in a fixed order), the head's valid flag,
+// and the reuse decision of the next step (strict sim > gamma; NaN, i.e. no
 // similarity yet, never reuses).
 __global__ __launch_bounds__(kThreads) void decide_kernel(const DecideParams p) {
   __shared__ float red[3][kThreads / 64];
@@ -168,19 +193,22 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(const DecideParams p) 
     }
   }
   if (tid == 0) {
-    if (computed) {
-      p.cur[bh] ^= 1;
-      p.valid[bh] = 1;
-    }
+    if (computed) p.valid[bh] = 1;
     const float s = p.sim[bh];
     p.reuse_next[bh] = (p.valid[bh] && s > p.gamma) ? 1 : 0;
   }
 }
 
+// Per-head decisions made on the host, recorded for a step that launches no
+// attention over them: 1 - selected.
+__global__ __launch_bounds__(kThreads) void record_kernel(const HeadSel sel, uint8_t* rec, int n_heads, int hq) {
+  const int bh = blockIdx.x * kThreads + threadIdx.x;
+  if (bh < n_heads) rec[bh] = head_selected(sel, bh / hq, bh) ? 0 : 1;
+}
+
 __global__ __launch_bounds__(kThreads) void reset_kernel(const ResetParams p) {
   const int bh = blockIdx.x * kThreads + threadIdx.x;
   if (bh >= p.n_heads) return;
-  p.cur[bh] = 0;
   p.valid[bh] = 0;
   p.reuse[bh] = 0;
   p.reuse[p.n_heads + bh] = 0;
@@ -244,13 +272,30 @@ hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, h
 hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s) {
   const int blocks = p.batch * p.hq * p.row_chunks;
   if (blocks == 0) return hipSuccess;
-  if (head_dim == 64) hipLaunchKernelGGL(combine_kernel<64>, dim3(blocks), dim3(kCombineThreads), 0, s, p);
-  else hipLaunchKernelGGL(combine_kernel<128>, dim3(blocks), dim3(kCombineThreads), 0, s, p);
+  // one memory round trip per BATCH splits: the smallest batch that holds the
+  // largest split count this launch can see (the device plan's too)
+  int most = p.splits;
+  for (int n = 1; n <= p.dyn.groups; ++n) most = std::max(most, (int)p.dyn.splits[n]);
+  if (head_dim == 64) {
+    if (most <= 8) hipLaunchKernelGGL((combine_kernel<64, 8>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+    else if (most <= 16) hipLaunchKernelGGL((combine_kernel<64, 16>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<64, 32>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+  } else {
+    if (most <= 8) hipLaunchKernelGGL((combine_kernel<128, 8>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+    else if (most <= 16) hipLaunchKernelGGL((combine_kernel<128, 16>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<128, 32>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_decide(const DecideParams& p, hipStream_t s) {
   hipLaunchKernelGGL(decide_kernel, dim3(p.n_heads), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_record(const HeadSel& sel, uint8_t* rec, int n_heads, int hq, hipStream_t s) {
+  hipLaunchKernelGGL(record_kernel, dim3((n_heads + kThreads - 1) / kThreads), dim3(kThreads), 0, s, sel, rec, n_heads,
+                     hq);
   return hipGetLastError();
 }
 

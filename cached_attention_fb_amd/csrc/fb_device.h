@@ -76,16 +76,7 @@ __device__ __forceinline__ void record_decisions(const AttnParams& p) {
     p.reuse_rec[bh] = head_selected(p.sel, bh / p.hq, bh) ? 0 : 1;
 }
 
-// Merge launches under the cumulative threshold decided on the device: one
-// thread per sequence restarts its sum where a head recomputed this step and
-// adds this step's count where all reused.  No launch of the same step reads
-// the sums after this one.
-__device__ __forceinline__ void update_cum(const AttnParams& p, int b, int g, int rt) {
-  if (p.cum == nullptr || g != 0 || rt != 0 || threadIdx.x != 0) return;
-  bool any = false;
-  for (int h = 0; h < p.hq; ++h) any |= head_selected(p.sel, b, b * p.hq + h);
-  p.cum[b] = any ? 0 : p.cum[b] + p.cum_m[b];
-}
+
 
 // Groups (sequence, kv head) with at least one selected query head, as a bit
 // mask over the group index b*Hkv + g (groups <= 64), computed by every wave
@@ -108,18 +99,35 @@ struct AttnItem {
   int b, g, split, rt;
   int key_begin, key_end;
   bool ok;
+  bool internal;   // a fused step's block-internal item
 };
 __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial) {
   AttnItem it;
+  it.internal = false;
   int kps = p.keys_per_split;
+  const int int_count = partial ? p.int_count : 0;
+  if ((int)blockIdx.x < int_count) {   // a fused step's block-internal item (they come first)
+    int w = xcd_remap(blockIdx.x, int_count);
+    it.rt = w % p.row_tiles;
+    w /= p.row_tiles;
+    it.g = w % p.hkv;
+    it.b = w / p.hkv;
+    it.split = p.int_split;
+    it.key_begin = 0;
+    it.key_end = p.bs;
+    it.ok = true;
+    it.internal = true;
+    return it;
+  }
+  const int w0 = (int)blockIdx.x - int_count;   // index among the external items
   if (partial && p.dyn.groups > 0) {
     const uint64_t mask = active_groups(p.sel, p.dyn.groups, p.hq, p.hkv);
     const int n = __builtin_popcountll(mask);
     const int splits = n > 0 ? p.dyn.splits[n] : 1;
     const int items = n * p.row_tiles * splits;
-    it.ok = (int)blockIdx.x < items;
+    it.ok = w0 < items;
     if (!it.ok) return it;
-    int w = xcd_remap(blockIdx.x, items);
+    int w = xcd_remap(w0, items);
     it.rt = w % p.row_tiles;
     w /= p.row_tiles;
     it.split = w % splits;
@@ -132,7 +140,7 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
     const int tiles = (p.n_keys + kKeyTile - 1) / kKeyTile;
     kps = ((tiles + splits - 1) / splits) * kKeyTile;
   } else {
-    int w = xcd_remap(blockIdx.x, gridDim.x);
+    int w = xcd_remap(w0, (int)gridDim.x - int_count);
     it.rt = w % p.row_tiles;
     w /= p.row_tiles;
     it.split = w % p.splits;
@@ -157,13 +165,15 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
 // Tile list: tile v starts at key 64 * list[v] (the item's part of its group's
 // list); keys at or past n_phys hold no key, and an entry outside the
 // prefix's tiles maps to a tile with none (its loads stay in bounds).
+// MAYBE_LIST = false compiles the contiguous form only.
+template <bool MAYBE_LIST>
 struct TileMap {
   const int32_t* list;
   int key_begin;
   int lim;          // first key that holds no key
   int phys_tiles;
   __device__ __forceinline__ int key0(int v) const {
-    if (list == nullptr) return key_begin + v * kKeyTile;
+    if (!MAYBE_LIST || list == nullptr) return key_begin + v * kKeyTile;
     const int t = load_scalar(list + v);
     return (t >= 0 && t < phys_tiles) ? t * kKeyTile : lim;
   }
@@ -180,9 +190,11 @@ struct TileMap {
     return *cp;
   }
 };
-__device__ __forceinline__ TileMap tile_map(const AttnParams& p, int b, int g, int key_begin, int key_end) {
-  TileMap m;
-  if (p.tiles == nullptr) {
+template <bool MAYBE_LIST>
+__device__ __forceinline__ TileMap<MAYBE_LIST> tile_map(const AttnParams& p, const AttnItem& it) {
+  TileMap<MAYBE_LIST> m;
+  const int b = it.b, g = it.g, key_begin = it.key_begin, key_end = it.key_end;
+  if (!MAYBE_LIST || p.tiles == nullptr || it.internal) {
     m.list = nullptr;
     m.key_begin = key_begin;
     m.lim = key_end;
@@ -272,23 +284,18 @@ __device__ __forceinline__ void store_partial(const AttnParams& p, const f32x16 
 
 // External part of one row for the merge: the head's cached A_out columns of
 // this lane (16 float4 for D=128) and L_out; an empty part when the head holds
-// nothing.  Loaded in two steps so that no load waits on another early in a
-// kernel: load_state reads the head's flags (which slot is current, whether it
-// holds a value), load_data then reads that slot unconditionally (the slots
-// are always allocated) and `has` is applied only at the merge.
+// nothing.  The flag and the data are independent loads (the cache is always
+// allocated), so both can be in flight at once; `has` is applied only at the
+// merge.
 template <int D>
 struct ExtPart {
   f32x4 a[D / 8];
   float l;
-  int slot;
   bool has;
-  __device__ __forceinline__ void load_state(const AttnParams& p, int bh) {
-    has = p.valid[bh] != 0;
-    slot = p.cur[bh];
-  }
+  __device__ __forceinline__ void load_state(const AttnParams& p, int bh) { has = p.valid[bh] != 0; }
   __device__ __forceinline__ void load_data(const AttnParams& p, int64_t grow, int hl) {
-    l = p.slot_l[slot * p.slot_l_stride + grow];
-    const float* ao = p.slot_o + slot * p.slot_o_stride + grow * D;
+    l = p.slot_l[grow];
+    const float* ao = p.slot_o + grow * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll

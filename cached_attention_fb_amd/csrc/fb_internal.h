@@ -67,27 +67,30 @@ struct AttnParams {
   int32_t grid;           // workgroups; 0: batch * hkv * splits * row_tiles
   int32_t splits;         // key ranges per group
   int32_t keys_per_split; // multiple of kKeyTile; with a device plan, the longest range it may pick
+  int32_t ring_keys;      // longest key range of any item of the launch (LDS ring sizing)
   float scale_log2;       // softmax scale * log2(e)
   HeadSel sel;
   DynPlan dyn;            // partial mode only
+  // Fused step (partial mode): the first int_count work items (B*Hkv*row_tiles,
+  // or 0) attend the block's own keys (kblk/vblk [B][Hkv][Bs][D], every head,
+  // no tile list) and store their partial at split index int_split; the
+  // external items follow.
+  const void* kblk;
+  const void* vblk;
+  int32_t int_count;
+  int32_t int_split;
   // partial epilogue: normalised A and natural-log L per split
   float* part_o;          // [splits][B][Hq][Bs][D]
   float* part_l;          // [splits][B][Hq][Bs]
   int64_t part_o_stride, part_l_stride;
-  // merge epilogue
-  const float* slot_o;    // [2][B][Hq][Bs][D]
-  const float* slot_l;    // [2][B][Hq][Bs]
-  int64_t slot_o_stride, slot_l_stride;
-  const uint8_t* cur;     // [B][Hq] current slot
+  // merge epilogue: the cached external part (or, sparse steps, the total)
+  const float* slot_o;    // [B][Hq][Bs][D]
+  const float* slot_l;    // [B][Hq][Bs]
   const uint8_t* valid;   // [B][Hq]
   void* out;              // [B][Hq][Bs][D]
   // [B][Hq] or null: 1 - selected(b, h) is recorded (merge: by the head's own
   // rows; partial: every head, by the first workgroup, for the launches after)
   uint8_t* reuse_rec;
-  // merge, cumulative threshold on the device: cum[b] restarts at 0 when a
-  // head of b was selected (recomputed), else grows by m[b]
-  int32_t* cum;
-  const int32_t* cum_m;
 };
 
 struct CombineParams {
@@ -97,18 +100,32 @@ struct CombineParams {
   int32_t splits, batch, hq, hkv, bs, row_chunks;
   HeadSel sel;
   DynPlan dyn;            // the external launch's plan (split count from the same active groups)
-  float* slot_o;
-  float* slot_l;
-  int64_t slot_o_stride, slot_l_stride;
-  uint8_t* cur;
+  float* slot_o;          // [B][Hq][Bs][D] the cache, refreshed in place
+  float* slot_l;          // [B][Hq][Bs]
   uint8_t* valid;
-  int32_t to_other_slot;  // 1: write slot cur^1 and sum similarity terms (gamma)
+  // 1 (gamma): before a value is replaced, sum <A_new, A_old>, |A_new|^2,
+  // |A_old|^2 over the workgroup's rows for the similarity (each lane reads
+  // the old value it then overwrites)
+  int32_t sim_terms;
   float* cos_part;        // [B*Hq][row_chunks][3]
   // Total mode (tot_o not null): the fold starts from the head's cached part
-  // (slot cur, when valid) and the result goes to tot_o [B][Hq][Bs][D] /
+  // (when valid) and the result goes to tot_o [B][Hq][Bs][D] /
   // tot_l [B][Hq][Bs]; the cache and its flags are left as they are.
   float* tot_o;
   float* tot_l;
+  // Output mode (out not null; every head): after the external part (the
+  // fold of the splits for a selected head, else its cached part, or the
+  // total mode's sum) fold in the block-internal partial at split index
+  // int_split and store the step's output [B][Hq][Bs][D] in the working dtype
+  // (out_bf16); the cache is written only for selected heads, the total
+  // buffer not at all.
+  void* out;
+  int32_t out_bf16;
+  int32_t int_split;
+  // cumulative threshold decided on the device: cum[b] restarts at 0 when a
+  // head of b was selected (recomputed), else grows by cum_m[b]
+  int32_t* cum;
+  const int32_t* cum_m;
 };
 
 // Tile list of the prefix keys a sparse selection leaves out.
@@ -127,7 +144,6 @@ struct DecideParams {
   int32_t group;          // 1: a similarity per head; G = Hq/Hkv: one per kv group (its heads' terms summed)
   const uint8_t* reuse_now;  // decisions applied at this step
   uint8_t* reuse_next;       // decisions for the next step
-  uint8_t* cur;
   uint8_t* valid;
   float* sim;
   const float* cos_part;
@@ -138,7 +154,6 @@ struct ResetParams {
   int32_t n_heads;
   int32_t batch;
   int32_t* cum;           // [B] or null
-  uint8_t* cur;
   uint8_t* valid;
   uint8_t* reuse;         // [2][B*Hq]
   float* sim;
@@ -152,5 +167,6 @@ hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s);
 hipError_t launch_decide(const DecideParams& p, hipStream_t s);
 hipError_t launch_reset(const ResetParams& p, hipStream_t s);
 hipError_t launch_complement(const ComplementParams& p, hipStream_t s);
+hipError_t launch_record(const HeadSel& sel, uint8_t* rec, int n_heads, int hq, hipStream_t s);
 
 }  // namespace fbk

@@ -8,7 +8,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "fb.h"
@@ -76,18 +78,20 @@ struct fb_cache {
   int32_t dyn_keys = -1;
   int dyn_grid = 0;      // workgroups of the largest item count over the plan
   int dyn_kps = 0;       // longest key range of the plan
+  int dyn_co = 0;        // co-scheduled workgroups the plan was made for
+  // split counts chosen so far: (keys, active groups, co workgroups, their tiles)
+  std::map<std::tuple<int, int, int, int>, int> split_memo;
   int n_cu = 256;        // compute units of the device
   float scale = 0.0f;
   size_t bytes = 0;
   // device memory
-  float* slot_o = nullptr;   // [2][B][Hq][Bs][D]
-  float* slot_l = nullptr;   // [2][B][Hq][Bs]
-  uint8_t* cur = nullptr;    // [B][Hq]
+  float* slot_o = nullptr;   // [B][Hq][Bs][D] cached A_out
+  float* slot_l = nullptr;   // [B][Hq][Bs]    cached L_out
   uint8_t* valid = nullptr;  // [B][Hq]
   uint8_t* reuse = nullptr;  // [2][B][Hq], indexed by step parity
   float* sim = nullptr;      // [B][Hq]
-  float* part_o = nullptr;   // [splits_cap][B][Hq][Bs][D]
-  float* part_l = nullptr;   // [splits_cap][B][Hq][Bs]
+  float* part_o = nullptr;   // [splits_cap + 1][B][Hq][Bs][D] (the last: a fused step's block-internal part)
+  float* part_l = nullptr;   // [splits_cap + 1][B][Hq][Bs]
   float* cos_part = nullptr; // [B][Hq][row_chunks][3]
   int32_t* cum = nullptr;    // [B] cumulative rule decided on the device: updated tokens since b's last computation
   float* tot_o = nullptr;    // [B][Hq][Bs][D] sparse steps: cached part merged with the kept keys' part
@@ -137,30 +141,70 @@ fb_status check_config(const fb_config* cfg) {
   return FB_OK;
 }
 
+// Time in tiles of a launch whose first co_items workgroups take co_tiles
+// tiles each and whose ext_wgs others take `per`: every CU runs one workgroup
+// at a time and takes the next one (in launch order) as it frees up.
+long span_with_co_items(int n_cu, long co_items, long co_tiles, long ext_wgs, long per) {
+  std::map<long, long> free_at;   // time -> CUs that free up then
+  free_at[0] = n_cu;
+  long qi = co_items, qe = ext_wgs, end = 0;
+  while (qi + qe > 0 && !free_at.empty()) {
+    const auto it = free_at.begin();
+    const long t = it->first;
+    long n = it->second;
+    free_at.erase(it);
+    const long a = std::min(n, qi);
+    if (a > 0) {
+      free_at[t + co_tiles] += a;
+      qi -= a;
+      n -= a;
+      end = std::max(end, t + co_tiles);
+    }
+    const long b = std::min(n, qe);
+    if (b > 0) {
+      free_at[t + per] += b;
+      qe -= b;
+      end = std::max(end, t + per);
+    }
+  }
+  return end;
+}
+
 // Number of prefix chunks.  Each (group, row tile, chunk) is one workgroup
 // and each CU runs one at a time, so the time goes as
-// ceil(workgroups / CUs) x tiles per chunk.  Take the smallest chunk count
-// within 2 % of the best such time (more chunks mean more partial traffic),
-// with at least two 64-key tiles per chunk and at most the scratch capacity.
-int choose_splits(const fb_cache* c, int n_keys, int active_groups) {
+// ceil(workgroups / CUs) x tiles per chunk (with a fused step's
+// block-internal workgroups in the same launch: as span_with_co_items
+// gives).  Take the smallest chunk count within 2 % of the best such time
+// (more chunks mean more partial traffic), with at least two 64-key tiles
+// per chunk and at most the scratch capacity.
+int choose_splits(fb_cache* c, int n_keys, int active_groups, int co_items = 0, int co_tiles = 0) {
   const int tiles = (n_keys + fbk::kKeyTile - 1) / fbk::kKeyTile;
   if (tiles <= 1) return 1;
   int want;
   if (c->cfg.kv_splits > 0) {
     want = c->cfg.kv_splits;
   } else {
+    const auto key = std::make_tuple(n_keys, active_groups, co_items, co_tiles);
+    const auto hit = c->split_memo.find(key);
+    if (hit != c->split_memo.end()) return hit->second;
     const int base = std::max(1, active_groups * c->row_tiles);
     const int smax = std::max(1, std::min({tiles / 2, c->splits_cap, fbk::kMaxSplits}));
     // makespan in tiles: rounds of workgroups x tiles per chunk, after
     // rounding the chunks to whole tiles
     auto span = [&](int sp) {
       const int per = (tiles + sp - 1) / sp, eff = (tiles + per - 1) / per;
+      if (co_items > 0) return (double)span_with_co_items(c->n_cu, co_items, co_tiles, (long)base * eff, per);
       return (double)((base * eff + c->n_cu - 1) / c->n_cu) * per;
     };
     double best = 1e30;
     for (int sp = 1; sp <= smax; ++sp) best = std::min(best, span(sp));
     want = 1;
     while (want < smax && span(want) > 1.02 * best) ++want;
+    want = std::max(1, std::min({want, tiles, c->splits_cap}));
+    const int tiles_per = (tiles + want - 1) / want;
+    const int sp = (tiles + tiles_per - 1) / tiles_per;   // no empty chunk
+    c->split_memo[key] = sp;
+    return sp;
   }
   want = std::max(1, std::min({want, tiles, c->splits_cap}));
   const int tiles_per = (tiles + want - 1) / want;
@@ -207,8 +251,8 @@ fbk::HeadSel all_heads(const fb_cache* c) {
 // scratch allows at most max(static choice, kDynSplitCap) splits.
 constexpr int kDynSplitCap = 16;
 bool dyn_possible(const fb_cache* c) { return c->cfg.batch * c->cfg.n_kv_heads <= fbk::kDynMaxGroups; }
-void plan_dyn(fb_cache* c, int n_keys) {
-  if (c->dyn_keys == n_keys) return;
+void plan_dyn(fb_cache* c, int n_keys, int co_items = 0, int co_tiles = 0) {
+  if (c->dyn_keys == n_keys && c->dyn_co == co_items) return;
   const int groups = c->cfg.batch * c->cfg.n_kv_heads;
   const int tiles = (n_keys + fbk::kKeyTile - 1) / fbk::kKeyTile;
   c->dyn.groups = groups;
@@ -216,13 +260,14 @@ void plan_dyn(fb_cache* c, int n_keys) {
   c->dyn_grid = 0;
   int min_splits = fbk::kMaxSplits;
   for (int n = 1; n <= groups; ++n) {
-    const int sp = choose_splits(c, n_keys, n);
+    const int sp = choose_splits(c, n_keys, n, co_items, co_tiles);
     c->dyn.splits[n] = (uint8_t)sp;
     c->dyn_grid = std::max(c->dyn_grid, n * c->row_tiles * sp);
     min_splits = std::min(min_splits, sp);
   }
   c->dyn_kps = std::max(1, (tiles + min_splits - 1) / min_splits) * fbk::kKeyTile;
   c->dyn_keys = n_keys;
+  c->dyn_co = co_items;
 }
 
 fbk::AttnParams attn_common(const fb_cache* c, const void* q, int waves, int ksplit) {
@@ -238,6 +283,7 @@ fbk::AttnParams attn_common(const fb_cache* c, const void* q, int waves, int ksp
   p.bs = c->cfg.block_size;
   p.rows = c->rows;
   p.scale_log2 = c->scale * 1.4426950408889634f;
+  p.int_count = 0;   // no block-internal items unless a fused step adds them
   return p;
 }
 
@@ -251,15 +297,28 @@ struct KeySet {
 };
 KeySet dense_keys(int32_t n) { return KeySet{n, nullptr, 0, n}; }
 
+// Options of an external launch and its split combine.
+struct ExtOpts {
+  bool gamma = false;        // the combine sums similarity terms as it replaces cached values
+  uint8_t* rec = nullptr;    // the attention launch records its per-head decisions, the combine follows them
+  bool to_total = false;     // the combine adds the cached part (sparse steps' kept keys)
+  // fused step: the attention launch also runs the block-internal items and
+  // the combine writes the step's output (every head)
+  const void* kblk = nullptr;
+  const void* vblk = nullptr;
+  void* out = nullptr;
+  const int32_t* cum_m = nullptr;   // cumulative threshold decided on the device
+};
+
 // External attention over a key set for the heads `sel` selects, and the
-// split combine into the cache.  rec != null: the attention launch records
-// its per-head decisions there and the combine selects from that record.
-// to_total: the combine adds the head's cached part and writes the total
-// buffer instead (the cache is not touched).
+// split combine into the cache (or, to_total, the total buffer).  A fused
+// step appends the block-internal items to the same launch and has the
+// combine merge them in and store the output, so one attention launch and
+// one combine make the whole step.
 fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* vp, const KeySet& ks,
-                       const fbk::HeadSel& sel, int active_groups, bool gamma, hipStream_t s,
-                       uint8_t* rec = nullptr, bool to_total = false) {
+                       const fbk::HeadSel& sel, int active_groups, hipStream_t s, const ExtOpts& o) {
   const int32_t n = ks.n_keys;
+  const bool fused = o.out != nullptr;
   fbk::AttnParams p = attn_common(c, q, c->ext_waves, c->ext_ksplit);
   p.k = kp;
   p.v = vp;
@@ -268,33 +327,48 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   p.tiles = ks.tiles;
   p.tiles_stride = ks.stride;
   p.n_phys = ks.n_phys;
-  p.splits = choose_splits(c, n, active_groups);
+  // a fused step's block-internal workgroups share the launch (and the CUs)
+  const int co_items = fused ? c->cfg.batch * c->cfg.n_kv_heads * p.row_tiles : 0;
+  const int co_tiles = (c->cfg.block_size + fbk::kKeyTile - 1) / fbk::kKeyTile;
+  p.splits = choose_splits(c, n, active_groups, co_items, co_tiles);
   const int tiles = (n + fbk::kKeyTile - 1) / fbk::kKeyTile;
   p.keys_per_split = std::max(1, (tiles + p.splits - 1) / p.splits) * fbk::kKeyTile;
+  int ext_items = c->cfg.batch * c->cfg.n_kv_heads * p.splits * p.row_tiles;
   if ((sel.flags != nullptr || sel.m != nullptr) && dyn_possible(c) && n > 0) {
-    plan_dyn(c, n);   // heads chosen on the device: the split count follows how many groups it selects
+    plan_dyn(c, n, co_items, co_tiles);   // heads chosen on the device: the split count follows how many groups it selects
     p.dyn = c->dyn;
-    p.grid = c->dyn_grid;
+    ext_items = c->dyn_grid;
     p.keys_per_split = c->dyn_kps;   // the longest range the plan may pick (LDS sizing)
   } else if (sel.flags == nullptr && sel.m == nullptr && dyn_possible(c) && n > 0 &&
              active_groups < c->cfg.batch * c->cfg.n_kv_heads) {
     // some sequences chosen on the host: enumerate only their groups, so the
     // work spreads over every XCD instead of the slice of the grid they own
-    plan_dyn(c, n);
+    plan_dyn(c, n, co_items, co_tiles);
     p.dyn = c->dyn;
-    p.grid = active_groups * p.row_tiles * p.splits;   // p.splits == dyn.splits[active_groups]
+    ext_items = active_groups * p.row_tiles * p.splits;   // p.splits == dyn.splits[active_groups]
+  }
+  const bool skip_ext = o.to_total && n == 0;   // nothing kept: the total is the cached part
+  if (skip_ext) ext_items = 0;
+  p.ring_keys = p.keys_per_split;
+  p.grid = ext_items;
+  if (fused) {
+    p.kblk = o.kblk;
+    p.vblk = o.vblk;
+    p.int_count = c->cfg.batch * c->cfg.n_kv_heads * p.row_tiles;
+    p.int_split = c->splits_cap;
+    p.grid = ext_items + p.int_count;
+    p.ring_keys = std::max(p.ring_keys, ((c->cfg.block_size + fbk::kKeyTile - 1) / fbk::kKeyTile) * fbk::kKeyTile);
   }
   p.sel = sel;
-  p.reuse_rec = rec;
+  p.reuse_rec = o.rec;
   p.part_o = c->part_o;
   p.part_l = c->part_l;
   p.part_o_stride = elems_per_slot(c->cfg);
   p.part_l_stride = rows_per_slot(c->cfg);
   ProfRec r;
   hipError_t e = hipSuccess;
-  const bool skip_attn = to_total && n == 0;   // nothing kept: the total is the cached part
-  if (!skip_attn) {
-    prof_begin(c, s, &r, to_total ? 5 : 0);
+  if (p.grid > 0) {
+    prof_begin(c, s, &r, o.to_total ? 5 : 0);
     e = fbk::launch_attn(c->cfg.dtype, c->cfg.head_dim, fbk::kModePartial, p, s);
     prof_end(c, s, &r);
     if (e != hipSuccess) return hip_fail(e, "external attention launch");
@@ -305,7 +379,7 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   cp.part_l = c->part_l;
   cp.part_o_stride = p.part_o_stride;
   cp.part_l_stride = p.part_l_stride;
-  cp.splits = skip_attn ? 0 : p.splits;
+  cp.splits = skip_ext ? 0 : p.splits;
   cp.batch = c->cfg.batch;
   cp.hq = c->cfg.n_q_heads;
   cp.hkv = c->cfg.n_kv_heads;
@@ -313,33 +387,40 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   cp.bs = c->cfg.block_size;
   cp.row_chunks = c->row_chunks;
   cp.sel = sel;
-  if (rec != nullptr) {
+  if (o.rec != nullptr) {
     cp.sel = all_heads(c);
-    cp.sel.flags = rec;
+    cp.sel.flags = o.rec;
     cp.sel.flags_select = 0;
   }
   cp.slot_o = c->slot_o;
   cp.slot_l = c->slot_l;
-  cp.slot_o_stride = elems_per_slot(c->cfg);
-  cp.slot_l_stride = rows_per_slot(c->cfg);
-  cp.cur = c->cur;
   cp.valid = c->valid;
-  cp.to_other_slot = gamma ? 1 : 0;
+  cp.sim_terms = o.gamma ? 1 : 0;
   cp.cos_part = c->cos_part;
-  if (to_total) {
+  if (o.to_total) {
     cp.tot_o = c->tot_o;
     cp.tot_l = c->tot_l;
   }
-  prof_begin(c, s, &r, to_total ? 6 : 1);
+  if (fused) {
+    cp.out = o.out;
+    cp.out_bf16 = c->cfg.dtype == FB_BF16 ? 1 : 0;
+    cp.int_split = c->splits_cap;
+  }
+  if (o.cum_m != nullptr) {
+    cp.cum = c->cum;
+    cp.cum_m = o.cum_m;
+  }
+  prof_begin(c, s, &r, o.to_total ? 6 : 1);
   e = fbk::launch_combine(c->cfg.head_dim, cp, s);
   prof_end(c, s, &r);
   if (e != hipSuccess) return hip_fail(e, "split combine launch");
   return FB_OK;
 }
 
+// Block-internal attention merged with the cached external part, one launch:
+// the step when no head recomputes (and fb_internal_attn_merge).
 fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* vb, void* out,
-                       const fbk::HeadSel& rec_sel, uint8_t* reuse_rec, hipStream_t s,
-                       const int32_t* cum_m = nullptr, bool from_total = false) {
+                       const fbk::HeadSel& rec_sel, uint8_t* reuse_rec, hipStream_t s) {
   fbk::AttnParams p = attn_common(c, q, c->int_waves, c->int_ksplit);
   p.k = kb;
   p.v = vb;
@@ -347,25 +428,13 @@ fb_status run_internal(fb_cache* c, const void* q, const void* kb, const void* v
   p.n_keys = c->cfg.block_size;
   p.splits = 1;
   p.keys_per_split = ((c->cfg.block_size + fbk::kKeyTile - 1) / fbk::kKeyTile) * fbk::kKeyTile;
+  p.ring_keys = p.keys_per_split;
   p.sel = rec_sel;
   p.slot_o = c->slot_o;
   p.slot_l = c->slot_l;
-  p.slot_o_stride = elems_per_slot(c->cfg);
-  p.slot_l_stride = rows_per_slot(c->cfg);
-  if (from_total) {   // the external part is the total buffer (every head holds one)
-    p.slot_o = c->tot_o;
-    p.slot_l = c->tot_l;
-    p.slot_o_stride = 0;
-    p.slot_l_stride = 0;
-  }
-  p.cur = c->cur;
   p.valid = c->valid;
   p.out = out;
   p.reuse_rec = reuse_rec;
-  if (cum_m != nullptr) {
-    p.cum = c->cum;
-    p.cum_m = cum_m;
-  }
   ProfRec r;
   prof_begin(c, s, &r, 2);
   hipError_t e = fbk::launch_attn(c->cfg.dtype, c->cfg.head_dim, fbk::kModeMerge, p, s);
@@ -379,7 +448,6 @@ fb_status run_reset(fb_cache* c, hipStream_t s) {
   rp.n_heads = c->cfg.batch * c->cfg.n_q_heads;
   rp.batch = c->cfg.batch;
   rp.cum = c->cum;
-  rp.cur = c->cur;
   rp.valid = c->valid;
   rp.reuse = c->reuse;
   rp.sim = c->sim;
@@ -399,8 +467,8 @@ fb_status run_reset(fb_cache* c, hipStream_t s) {
 }
 
 void free_all(fb_cache* c) {
-  void* ptrs[] = {c->slot_o, c->slot_l, c->cur,   c->valid, c->reuse, c->sim,  c->part_o,
-                  c->part_l, c->cos_part, c->cum, c->tot_o, c->tot_l, c->comp};
+  void* ptrs[] = {c->slot_o, c->slot_l,   c->valid, c->reuse, c->sim,   c->part_o,
+                  c->part_l, c->cos_part, c->cum,   c->tot_o, c->tot_l, c->comp};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& r : c->prof_recs) {
@@ -466,6 +534,7 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
     c->splits_cap = cap;
   }
   if (cfg->kv_splits > 0) c->splits_cap = std::max(c->splits_cap, std::min(cfg->kv_splits, fbk::kMaxSplits));
+  c->split_memo.clear();   // those choices were made before the cap was known
 
   c->comp_stride = std::max(1, (cfg->max_prefix + fbk::kKeyTile - 1) / fbk::kKeyTile);
   const int64_t nh = (int64_t)cfg->batch * cfg->n_q_heads;
@@ -474,14 +543,13 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
     void** p;
     size_t n;
   } plan[] = {
-      {(void**)&c->slot_o, 2 * so},
-      {(void**)&c->slot_l, 2 * sl},
-      {(void**)&c->cur, (size_t)nh},
+      {(void**)&c->slot_o, so},
+      {(void**)&c->slot_l, sl},
       {(void**)&c->valid, (size_t)nh},
       {(void**)&c->reuse, (size_t)(2 * nh)},
       {(void**)&c->sim, (size_t)nh * sizeof(float)},
-      {(void**)&c->part_o, (size_t)c->splits_cap * so},
-      {(void**)&c->part_l, (size_t)c->splits_cap * sl},
+      {(void**)&c->part_o, (size_t)(c->splits_cap + 1) * so},   // + the block-internal partial of a fused step
+      {(void**)&c->part_l, (size_t)(c->splits_cap + 1) * sl},
       {(void**)&c->cos_part, (size_t)nh * c->row_chunks * 3 * sizeof(float)},
       {(void**)&c->cum, (size_t)cfg->batch * sizeof(int32_t)},
       {(void**)&c->tot_o, so},
@@ -543,7 +611,7 @@ fb_status fb_external_attn(fb_cache* c, const void* q_blk, const void* k_prefix,
   sel.flags = head_mask;
   sel.flags_select = 1;
   fb_status st = run_external(c, q_blk, k_prefix, v_prefix, dense_keys(prefix_len), sel,
-                              c->cfg.batch * c->cfg.n_kv_heads, false, (hipStream_t)stream);
+                              c->cfg.batch * c->cfg.n_kv_heads, (hipStream_t)stream, ExtOpts{});
   if (st != FB_OK) return st;
   std::fill(c->host_valid.begin(), c->host_valid.end(), head_mask ? 0 : 1);
   return ok();
@@ -657,22 +725,69 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
   }
 
   fb_status st = FB_OK;
-  fbk::HeadSel rec_sel = sel;     // what the merge launch records or follows
-  uint8_t* rec = nullptr;         // decisions the merge launch records (host threshold)
-  const int32_t* cum_m = nullptr;
+  const int groups = B * c->cfg.n_kv_heads;
+  // The step's external part: which heads recompute, and how (see each branch).
+  ExtOpts eo;
+  eo.kblk = k_blk;
+  eo.vblk = v_blk;
+  eo.out = out;   // fused: one attention launch and one combine for the whole step
+  fbk::HeadSel ext_sel = sel;
+  int ext_active = active * c->cfg.n_kv_heads;
   if (gamma_like) {
-    sel = all_heads(c);
-    sel.flags = reuse_now;
-    sel.flags_select = 0;   // compute the heads not marked for reuse
-    st = run_external(c, q_blk, k_prefix, v_prefix, cached, sel, B * c->cfg.n_kv_heads, true, s);
+    ext_sel = all_heads(c);
+    ext_sel.flags = reuse_now;
+    ext_sel.flags_select = 0;   // compute the heads not marked for reuse
+    ext_active = groups;
+    eo.gamma = true;
+  } else if (dev_m) {
+    // threshold decided in the attention launch from the counts in device
+    // memory; it records the decisions, the combine follows them
+    ext_sel = all_heads(c);
+    ext_sel.m = pa->n_updated_dev;
+    ext_sel.tau = pa->tau;
+    ext_sel.valid = c->valid;
+    ext_sel.cum = pa->policy == FB_POLICY_TAU_CUM ? c->cum : nullptr;
+    ext_active = groups;
+    eo.rec = reuse_now;
+    if (pa->policy == FB_POLICY_TAU_CUM) eo.cum_m = pa->n_updated_dev;
+  } else {
+    ext_sel.flags = nullptr;
+    ext_sel.flags_select = 1;
+    eo.rec = reuse_now;   // the host's per-sequence decisions, recorded per head
+  }
+  if (!sp) {
+    if (!gamma_like && !dev_m && active == 0) {
+      // every head reuses (known on the host): block-internal attention merged
+      // with the cache, one launch
+      st = run_internal(c, q_blk, k_blk, v_blk, out, ext_sel, reuse_now, s);
+    } else {
+      st = run_external(c, q_blk, k_prefix, v_prefix, cached, ext_sel, ext_active, s, eo);
+    }
     if (st != FB_OK) return st;
+  } else {
+    // sparse: the left-out tiles' part into the cache (recomputing heads),
+    // then the kept tiles for every head folded with it, the block-internal
+    // part and the output
+    ExtOpts ro;
+    ro.gamma = eo.gamma;
+    ro.rec = eo.rec;
+    ro.cum_m = eo.cum_m;   // the sums follow the decisions this combine selects by
+    if (gamma_like || dev_m || active > 0) {
+      st = run_external(c, q_blk, k_prefix, v_prefix, cached, ext_sel, ext_active, s, ro);
+      if (st != FB_OK) return st;
+    } else {
+      // nothing recomputes: record the decisions (the kept launch records none)
+      hipError_t e = fbk::launch_record(ext_sel, reuse_now, (int)nh, c->cfg.n_q_heads, s);
+      if (e != hipSuccess) return hip_fail(e, "decision record launch");
+    }
+  }
+  if (gamma_like) {   // similarity and the next step's decisions
     fbk::DecideParams dp{};
     dp.n_heads = (int32_t)nh;
     dp.hq = c->cfg.n_q_heads;
     dp.row_chunks = c->row_chunks;
     dp.reuse_now = reuse_now;
     dp.reuse_next = reuse_next;
-    dp.cur = c->cur;
     dp.valid = c->valid;
     dp.sim = c->sim;
     dp.cos_part = c->cos_part;
@@ -683,39 +798,17 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
     hipError_t e = fbk::launch_decide(dp, s);
     prof_end(c, s, &r);
     if (e != hipSuccess) return hip_fail(e, "decision launch");
-    rec_sel = sel;
-  } else if (dev_m) {
-    // threshold decided in the external launch from the counts in device
-    // memory; it records the decisions, the later launches follow them
-    sel = all_heads(c);
-    sel.m = pa->n_updated_dev;
-    sel.tau = pa->tau;
-    sel.valid = c->valid;
-    sel.cum = pa->policy == FB_POLICY_TAU_CUM ? c->cum : nullptr;
-    st = run_external(c, q_blk, k_prefix, v_prefix, cached, sel, B * c->cfg.n_kv_heads, false, s, reuse_now);
-    if (st != FB_OK) return st;
-    rec_sel = all_heads(c);
-    rec_sel.flags = reuse_now;
-    rec_sel.flags_select = 0;
-    if (pa->policy == FB_POLICY_TAU_CUM) cum_m = pa->n_updated_dev;
-  } else {
-    sel.flags = nullptr;
-    sel.flags_select = 1;
-    if (active > 0) {
-      st = run_external(c, q_blk, k_prefix, v_prefix, cached, sel, active * c->cfg.n_kv_heads, false, s);
-      if (st != FB_OK) return st;
-    }
-    rec_sel = sel;
-    rec = reuse_now;
   }
-  if (sp) {   // the kept tiles, afresh for every head, folded with the cached part
+  if (sp) {
     const KeySet kept{n_sel * fbk::kKeyTile, sp->sel, n_sel, prefix_len};
-    st = run_external(c, q_blk, k_prefix, v_prefix, kept, all_heads(c), B * c->cfg.n_kv_heads, false, s,
-                      nullptr, true);
+    ExtOpts ko;
+    ko.to_total = true;
+    ko.kblk = k_blk;
+    ko.vblk = v_blk;
+    ko.out = out;
+    st = run_external(c, q_blk, k_prefix, v_prefix, kept, all_heads(c), groups, s, ko);
     if (st != FB_OK) return st;
   }
-  st = run_internal(c, q_blk, k_blk, v_blk, out, rec_sel, rec, s, cum_m, sp != nullptr);
-  if (st != FB_OK) return st;
   if (!gamma_like && !dev_m) {
     std::fill(c->host_valid.begin(), c->host_valid.end(), 1);
     for (int b = 0; b < B; ++b)   // TAU_CUM: the sum restarts where a sequence recomputed
@@ -768,22 +861,9 @@ fb_status fb_cache_read(const fb_cache* c, int32_t field, void* host_dst, size_t
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "stream synchronise");
-  if (field == FB_FIELD_A_OUT || field == FB_FIELD_L_OUT) {
-    std::vector<uint8_t> cur(nh);
-    e = hipMemcpy(cur.data(), c->cur, nh, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_fail(e, "copy");
-    const bool is_o = field == FB_FIELD_A_OUT;
-    const int64_t per_head = is_o ? (int64_t)c->cfg.block_size * c->cfg.head_dim : c->cfg.block_size;
-    const float* base = is_o ? c->slot_o : c->slot_l;
-    const int64_t slot_stride = is_o ? so : sl;
-    for (int64_t bh = 0; bh < nh; ++bh) {
-      e = hipMemcpy(static_cast<float*>(host_dst) + bh * per_head, base + cur[bh] * slot_stride + bh * per_head,
-                    per_head * sizeof(float), hipMemcpyDeviceToHost);
-      if (e != hipSuccess) return hip_fail(e, "copy");
-    }
-    return ok();
-  }
-  const void* src = field == FB_FIELD_SIM ? (const void*)c->sim
+  const void* src = field == FB_FIELD_A_OUT   ? (const void*)c->slot_o
+                    : field == FB_FIELD_L_OUT ? (const void*)c->slot_l
+                    : field == FB_FIELD_SIM   ? (const void*)c->sim
                     : field == FB_FIELD_VALID ? (const void*)c->valid
                                               : (const void*)(c->reuse + ((c->steps + 1) & 1) * nh);
   e = hipMemcpy(host_dst, src, want, hipMemcpyDeviceToHost);

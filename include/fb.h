@@ -97,11 +97,13 @@ typedef struct {
 
 typedef struct fb_cache fb_cache;   /* opaque; owns device memory (hipMalloc) */
 
-/* Allocate the A_out/L_out cache for `cfg` on the current device: two fp32
- * slots of A_out [B][Hq][Bs][D] and L_out [B][Hq][Bs] per head (the second
- * holds the previous A_out while a similarity is measured), per-head flags,
- * and scratch for split-prefix partial results sized for max_prefix.  The new
- * cache is in the reset state.  *out is set only on FB_OK.
+/* Allocate the A_out/L_out cache for `cfg` on the current device: fp32
+ * A_out [B][Hq][Bs][D] and L_out [B][Hq][Bs] (a recomputed head's value
+ * replaces the old one in place; under GAMMA the similarity is taken as it is
+ * replaced), per-head flags, scratch for split-prefix partial results sized
+ * for max_prefix, and for sparse steps a total buffer of the A_out size and
+ * the list of left-out prefix tiles.  The new cache is in the reset state.
+ * *out is set only on FB_OK.
  * Errors: FB_E_ARG (null), FB_E_DTYPE, FB_E_SHAPE, FB_E_UNSUPPORTED,
  * FB_E_NOMEM, FB_E_HIP (no device). */
 fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out);

@@ -3,9 +3,11 @@ graphs.
 
 With the updated-token counts in device memory (fb_policy_args.n_updated_dev)
 the external-attention launch decides per head and records the decisions for
-the launches after it.  These must equal the host's decisions bit for bit, and
-since the same kernels then run on the same split plan, so must every output;
-the oracle checks both.  A block recorded by stream capture (reset + every
+the launches after it.  These must equal the host's decisions bit for bit,
+and since the same kernels then refresh the cache on the same split plan, so
+must the cached parts; the outputs of steps where every head reuses may come
+from another kernel on the host path (one launch when the host knows it), so
+they agree to rounding; the oracle checks both.  A block recorded by stream capture (reset + every
 step) and replayed with other counts and with other work between the replays
 must reproduce, replay after replay, what the same steps give eagerly.
 """
@@ -42,7 +44,9 @@ def test_device_counts_match_host_and_oracle(name, prefix, policy):
     ref = H.run_oracle(inp, policy=policy)
     for i, (d, h, r) in enumerate(zip(dev, host, ref)):
         np.testing.assert_array_equal(d.reuse, h.reuse)
-        np.testing.assert_array_equal(d.out, h.out)
+        scale = float(np.max(np.abs(h.out)))
+        ulp = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -20   # one rounding of the output
+        assert float(np.max(np.abs(d.out - h.out))) <= ulp * scale
         np.testing.assert_array_equal(d.a_out, h.a_out)
         np.testing.assert_array_equal(d.l_out, h.l_out)
         errs = H.compare_block(d, r, w.dtype, what=f"{name} {policy} device block {i}")
