@@ -14,8 +14,9 @@ Printed: one JSON line for the headline workload (the dLLM layer, batch 1,
 32/8 heads, prefix 8192, block 32).  ``value`` is the effective KV bandwidth:
 the prefix K/V bytes a recompute-every-step (ALWAYS) run would read, divided by
 the time taken under the workload's reuse policy.  ``roofline`` reports the
-external attention kernel's algorithmic bytes per launch over its average
-launch duration (HIP events around each launch on its stream, in a profiled
+recompute step's attention launch (block-external split-KV items plus the
+block-internal items it carries): algorithmic bytes per launch over its
+average launch duration (HIP events around each launch on its stream, in a profiled
 pass of the same steps under ALWAYS).  ``cpu_baseline`` times the float64
 oracle on the host cores.  ``workloads`` holds the same step and kernel
 figures, from fewer steps, for the other workloads.
@@ -59,14 +60,18 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic(w, n_prefix):
-    """Algorithmic work of one full external attention: K+V read once per
-    (sequence, kv head), Q read, A_out (fp32) and L_out (fp32) written."""
+    """Algorithmic work of one recompute-step attention launch, which holds
+    the block-external attention of every head and (fused step) its
+    block-internal attention: prefix K+V read once per (sequence, kv head),
+    block K+V and Q read, and the two results (A, L in fp32) written.
+    Returns (prefix K/V bytes, bytes of the launch, flops of the launch)."""
     e = w.elem_bytes
     kv = 2 * w.batch * w.n_kv_heads * n_prefix * w.head_dim * e
+    kv_blk = 2 * w.batch * w.n_kv_heads * w.block * w.head_dim * e
     q = w.batch * w.n_q_heads * w.block * w.head_dim * e
-    out = w.batch * w.n_q_heads * w.block * (w.head_dim + 1) * 4
-    flops = 4.0 * w.batch * w.n_q_heads * w.block * n_prefix * w.head_dim
-    return kv, kv + q + out, flops
+    out = 2 * w.batch * w.n_q_heads * w.block * (w.head_dim + 1) * 4
+    flops = 4.0 * w.batch * w.n_q_heads * w.block * (n_prefix + w.block) * w.head_dim
+    return kv, kv + kv_blk + q + out, flops
 
 
 def roofline(w, ext_us, alg_bytes, alg_flops):
@@ -199,7 +204,7 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
 
     roof = roofline(w, ext_us, alg_bytes, alg_flops)
     roof["kernel"] = ("attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel") + \
-        " (block-external, split-KV partials)"
+        " (recompute step: block-external split-KV partials + block-internal items)"
     roof["avg_launch_us"] = round(ext_us, 3)
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["algorithmic_flops_per_launch"] = alg_flops
@@ -377,13 +382,10 @@ def sparse_bench(name, densities=(0.2, 0.3, 0.4), blocks=4, warmup=1):
             c.profile_enable(False)
         kern = {k: round(1e3 * v[1] / v[0], 3) for k, v in prof.items() if v[0]}
         kept_rows = min(n, n_sel * 64)
-        kept_kv = 2 * w.batch * w.n_kv_heads * kept_rows * w.head_dim * w.elem_bytes
-        q_b = w.batch * w.n_q_heads * w.block * w.head_dim * w.elem_bytes
-        out_b = w.batch * w.n_q_heads * w.block * (w.head_dim + 1) * 4
         kept_roof = None
-        if "sparse_kept" in kern:
-            kept_roof = roofline(w, kern["sparse_kept"], kept_kv + q_b + out_b,
-                                 4.0 * w.batch * w.n_q_heads * w.block * kept_rows * w.head_dim)
+        if "sparse_kept" in kern:   # the kept tiles' launch also carries the block-internal items
+            _, kept_bytes, kept_flops = algorithmic(w, kept_rows)
+            kept_roof = roofline(w, kern["sparse_kept"], kept_bytes, kept_flops)
         res["densities"][str(dens)] = {
             "kept_tiles": n_sel, "kept_fraction": round(n_sel * 64 / n, 4),
             "tau_us_per_layer_step": round(tau_us, 3), "always_us_per_layer_step": round(always_us, 3),
