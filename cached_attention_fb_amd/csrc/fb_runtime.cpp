@@ -300,7 +300,9 @@ KeySet dense_keys(int32_t n) { return KeySet{n, nullptr, 0, n}; }
 // Options of an external launch and its split combine.
 struct ExtOpts {
   bool gamma = false;        // the combine sums similarity terms as it replaces cached values
-  uint8_t* rec = nullptr;    // the attention launch records its per-head decisions, the combine follows them
+  uint8_t* rec = nullptr;    // the attention launch records its per-head decisions there
+  bool follow_rec = true;    // the combine selects by that record (decisions made on the device);
+                             // false: by `sel` itself (host decisions: no flag load before its work)
   bool to_total = false;     // the combine adds the cached part (sparse steps' kept keys)
   // fused step: the attention launch also runs the block-internal items and
   // the combine writes the step's output (every head)
@@ -387,7 +389,7 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   cp.bs = c->cfg.block_size;
   cp.row_chunks = c->row_chunks;
   cp.sel = sel;
-  if (o.rec != nullptr) {
+  if (o.rec != nullptr && o.follow_rec) {
     cp.sel = all_heads(c);
     cp.sel.flags = o.rec;
     cp.sel.flags_select = 0;
@@ -754,6 +756,7 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
     ext_sel.flags = nullptr;
     ext_sel.flags_select = 1;
     eo.rec = reuse_now;   // the host's per-sequence decisions, recorded per head
+    eo.follow_rec = false;
   }
   if (!sp) {
     if (!gamma_like && !dev_m && active == 0) {
@@ -771,6 +774,7 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
     ExtOpts ro;
     ro.gamma = eo.gamma;
     ro.rec = eo.rec;
+    ro.follow_rec = eo.follow_rec;
     ro.cum_m = eo.cum_m;   // the sums follow the decisions this combine selects by
     if (gamma_like || dev_m || active > 0) {
       st = run_external(c, q_blk, k_prefix, v_prefix, cached, ext_sel, ext_active, s, ro);
