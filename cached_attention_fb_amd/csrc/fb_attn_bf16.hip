@@ -260,6 +260,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   extern __shared__ char smem_raw[];
   FB_LDS char* lds = (FB_LDS char*)smem_raw;
 
+  prefetch_params(p);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rw = wave % ROWW, kh = wave / ROWW;
   const int rl = lane & 31, hl = lane >> 5;

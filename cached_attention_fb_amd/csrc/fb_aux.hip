@@ -28,6 +28,7 @@ template <int D, int BATCH>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p) {
   constexpr int kLpr = D / 4;
   constexpr int kRows = kCombineThreads / kLpr;
+  prefetch_params(p);
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / p.row_chunks, ch = blockIdx.x % p.row_chunks;
   const int b = bh / p.hq;

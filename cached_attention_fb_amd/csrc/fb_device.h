@@ -56,8 +56,21 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return x * q + min(x, r) + j;
 }
 
+// Touch every 64-byte line of a kernel's parameter block at once.  The
+// prologue reads its parameters with scalar loads that are each waited for
+// before a branch; without this they go to memory one round trip after
+// another, with it they hit the scalar cache after a single one.
+template <typename P>
+__device__ __forceinline__ void prefetch_params(const P& p) {
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(&p);
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(P) / 4); i += 16) acc ^= a[i];
+  asm volatile("" ::"s"(acc));
+}
+
 __device__ __forceinline__ bool head_selected(const HeadSel& s, int b, int bh) {
-  if (!((s.seq_bits[b >> 5] >> (b & 31)) & 1u)) return false;
+  if (!s.every_seq && !((s.seq_bits[b >> 5] >> (b & 31)) & 1u)) return false;
   if (s.m != nullptr) {   // threshold rule with the updated-token counts in device memory
     const int64_t upd = (int64_t)s.m[b] + (s.cum != nullptr ? s.cum[b] : 0);
     return !(s.valid[bh] != 0 && upd < s.tau);

@@ -24,6 +24,7 @@ constexpr int combine_rows(int head_dim) { return 4 * kCombineThreads / head_dim
 // unless the head holds a computed A_out (valid) and m[b] (+ cum[b] when cum
 // is not null) < tau.  m, cum and valid must not change during the launch.
 struct HeadSel {
+  int32_t every_seq;      // 1: every sequence's bit is set (the bits need not be read)
   uint32_t seq_bits[FB_MAX_BATCH / 32];
   const uint8_t* flags;
   int32_t flags_select;

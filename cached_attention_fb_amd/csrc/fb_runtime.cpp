@@ -241,6 +241,7 @@ void prof_end(fb_cache* c, hipStream_t s, ProfRec* r) {
 fbk::HeadSel all_heads(const fb_cache* c) {
   fbk::HeadSel h{};
   for (int b = 0; b < c->cfg.batch; ++b) h.seq_bits[b >> 5] |= 1u << (b & 31);
+  h.every_seq = 1;
   h.flags = nullptr;
   h.flags_select = 1;
   return h;
@@ -699,6 +700,7 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
       ++active;
     }
   }
+  sel.every_seq = active == B ? 1 : 0;
   DeviceGuard g(c->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "set device");
   hipStream_t s = (hipStream_t)stream;
