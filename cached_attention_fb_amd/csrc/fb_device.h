@@ -298,14 +298,15 @@ __device__ __forceinline__ void store_partial(const AttnParams& p, const f32x16 
 // External part of one row for the merge: the head's cached A_out columns of
 // this lane (16 float4 for D=128) and L_out; an empty part when the head holds
 // nothing.  The flag and the data are independent loads (the cache is always
-// allocated), so both can be in flight at once; `has` is applied only at the
-// merge.
+// allocated), so both can be in flight at once.  The flag is kept as the
+// loaded byte and tested only at the merge: converting it at once makes the
+// compiler wait for the load before anything else is issued.
 template <int D>
 struct ExtPart {
   f32x4 a[D / 8];
   float l;
-  bool has;
-  __device__ __forceinline__ void load_state(const AttnParams& p, int bh) { has = p.valid[bh] != 0; }
+  uint32_t valid;
+  __device__ __forceinline__ void load_state(const AttnParams& p, int bh) { valid = p.valid[bh]; }
   __device__ __forceinline__ void load_data(const AttnParams& p, int64_t grow, int hl) {
     l = p.slot_l[grow];
     const float* ao = p.slot_o + grow * D;
@@ -327,7 +328,10 @@ template <typename T, int D>
 __device__ __forceinline__ void merge_store(const AttnParams& p, const f32x16 (&o)[D / 32], float m, float ltot,
                                             const ExtPart<D>& ext, int64_t grow, int hl) {
   const float l_in = (m + log2f(ltot)) * kLn2;
-  const float l_out = ext.has ? ext.l : -INFINITY;
+  uint32_t valid = ext.valid;
+  asm volatile("" : "+v"(valid));   // keeps the test (and its wait for the load) here
+  const bool has = valid != 0;
+  const float l_out = has ? ext.l : -INFINITY;
   const float mm = fmaxf(l_out, l_in);
   const float w_out = fast_exp2((l_out - mm) * kLog2e);
   const float w_in = fast_exp2((l_in - mm) * kLog2e);
@@ -342,7 +346,7 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, const f32x16 (&
       f32x4 r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float a_out = ext.has ? ext.a[4 * dt + gq][e] : 0.0f;   // an empty slot may hold anything
+        const float a_out = has ? ext.a[4 * dt + gq][e] : 0.0f;   // an empty cache may hold anything
         r[e] = c_out * a_out + c_in * o[dt][4 * gq + e];
       }
       if constexpr (sizeof(T) == 2) {
