@@ -183,7 +183,9 @@ struct Pipe {
   __host__ __device__ static int q_offset(int ring) { return ring == kStages ? 2 * kStageBytes : ring * kStageBytes; }
 };
 
-template <int D, int WAVES>
+// AUX: cache policy of the DMA loads (2: non-temporal, for K/V that no other
+// workgroup of the launch reads again).
+template <int D, int WAVES, int AUX>
 __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, const bf16* vb, int tile0,
                                            int key_end, int wave, int lane) {
   using P = Pipe<D, WAVES>;
@@ -197,7 +199,7 @@ __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, c
     const int swz = tensor == 0 ? (key & (P::kCpr - 1)) : ((4 * key) & (P::kCpr - 4));
     const int gk = min(tile0 + key, key_end - 1);   // rows past the end: any valid row (masked later)
     const bf16* src = (tensor == 0 ? kb : vb) + (int64_t)gk * D + (pc ^ swz) * 8;
-    __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(stage + tensor * P::kTensorBytes + ii * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(stage + tensor * P::kTensorBytes + ii * 1024), 16, 0, AUX);
   }
 }
 
@@ -257,6 +259,11 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   constexpr int NH = 2 / KSPLIT;   // 32-key halves of a tile per wave
   using P = Pipe<D, WAVES>;
   constexpr int kDt = D / 32;
+  // Streaming K/V: in the partial launches of the short-block shapes a K/V
+  // tile is read by exactly one workgroup (one row tile per group), so the
+  // loads are marked non-temporal; frame-sized blocks re-read each tile from
+  // L2 for every row tile and keep the default policy.
+  constexpr int kAux = (MODE == kModePartial && (KSPLIT == 2 || ROWW == 1)) ? 2 : 0;
   extern __shared__ char smem_raw[];
   FB_LDS char* lds = (FB_LDS char*)smem_raw;
 
@@ -302,12 +309,12 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   if (kh == 0 && wave_live) issue_q<D>(q_lds, qg + (grow - rl) * D, p.rows - row0, lane);
   int issued;
   if (ntiles >= 2) {
-    issue_tile<D, WAVES>(lds, kb, vb, tm.key0(0), lim, wave, lane);
-    issue_tile<D, WAVES>(lds + P::kStageBytes, kb, vb, tm.key0(1), lim, wave, lane);
+    issue_tile<D, WAVES, kAux>(lds, kb, vb, tm.key0(0), lim, wave, lane);
+    issue_tile<D, WAVES, kAux>(lds + P::kStageBytes, kb, vb, tm.key0(1), lim, wave, lane);
     issued = 2;
     wait_vmcnt<P::kLpt>();   // tile 0 (and everything issued before it) landed
   } else if (ntiles == 1) {
-    issue_tile<D, WAVES>(lds, kb, vb, tm.key0(0), lim, wave, lane);
+    issue_tile<D, WAVES, kAux>(lds, kb, vb, tm.key0(0), lim, wave, lane);
     issued = 1;
     wait_vmcnt<0>();
   } else {
@@ -449,7 +456,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     // Refill after the compute, so that a stalled issue does not delay it:
     // the stage of tile t_i-1 is free (every wave passed the barrier above).
     for (; issued < ntiles && issued <= t_i + P::kStages - 1; ++issued)
-      issue_tile<D, WAVES>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, tm.key0(issued), lim, wave,
+      issue_tile<D, WAVES, kAux>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, tm.key0(issued), lim, wave,
                            lane);
   }
 
