@@ -239,13 +239,15 @@ __device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f3
       *reinterpret_cast<FB_LDS f32x4*>(st + rl * D + ((c ^ (rl & (kC - 1))) * 4)) = v4;
     }
   }
-  if (hl == 0 && rl < nrows) p.part_l[split * p.part_l_stride + grow0 + rl] = lse;
+  // streaming stores: the partials leave this launch for the combine, and
+  // kept out of L2 they need no write-back when the launch ends
+  if (hl == 0 && rl < nrows) __builtin_nontemporal_store(lse, p.part_l + split * p.part_l_stride + grow0 + rl);
   float* od = p.part_o + split * p.part_o_stride + grow0 * D;
 #pragma unroll
   for (int k = 0; k < 32 / kRowsPerOp; ++k) {
     const int r = k * kRowsPerOp + lane / kC, c = lane % kC;
     const f32x4 v = *reinterpret_cast<const FB_LDS f32x4*>(st + r * D + ((c ^ (r & (kC - 1))) * 4));
-    if (r < nrows) *reinterpret_cast<f32x4*>(od + (int64_t)r * D + 4 * c) = v;
+    if (r < nrows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(od + (int64_t)r * D + 4 * c));
   }
 }
 
