@@ -255,17 +255,14 @@ __device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f3
 template <int D, int ROWW>
 constexpr int xch_bytes() { return ROWW * (16 * (D / 32) + 2) * 64 * 4; }
 
-template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT, bool LIST>
+// AUX: cache policy of the K/V DMA loads (see issue_tile).
+template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT, bool LIST, int AUX>
 __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const AttnParams p) {
   constexpr int WAVES = ROWW * KSPLIT;
   constexpr int NH = 2 / KSPLIT;   // 32-key halves of a tile per wave
   using P = Pipe<D, WAVES>;
   constexpr int kDt = D / 32;
-  // Streaming K/V: in the partial launches of the short-block shapes a K/V
-  // tile is read by exactly one workgroup (one row tile per group), so the
-  // loads are marked non-temporal; frame-sized blocks re-read each tile from
-  // L2 for every row tile and keep the default policy.
-  constexpr int kAux = (MODE == kModePartial && (KSPLIT == 2 || ROWW == 1)) ? 2 : 0;
+  constexpr int kAux = AUX;
   extern __shared__ char smem_raw[];
   FB_LDS char* lds = (FB_LDS char*)smem_raw;
 
@@ -519,7 +516,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   }
 }
 
-template <int D, int ROWW, int KSPLIT, int MODE, bool PF, bool LIST>
+template <int D, int ROWW, int KSPLIT, int MODE, bool PF, bool LIST, int AUX>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   using P = Pipe<D, ROWW * KSPLIT>;
   const int blocks = p.grid > 0 ? p.grid : p.batch * p.hkv * p.splits * p.row_tiles;
@@ -530,7 +527,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
                                     KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -540,16 +537,25 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   int lds = std::max(ring * P::kStageBytes, P::q_offset(ring) + kQBytes);
   if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
   lds = std::max(lds, kStageOut);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST>), dim3(blocks), dim3(64 * ROWW * KSPLIT),
+  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX>), dim3(blocks), dim3(64 * ROWW * KSPLIT),
                      lds, s, p);
   return hipGetLastError();
 }
 
+// Streaming K/V: in a partial launch with one row tile per group every K/V
+// tile is read by exactly one workgroup, so its loads are marked
+// non-temporal (AUX 2); with several row tiles (frame-sized blocks) each tile
+// is re-read from L2 by every row tile and keeps the default policy.  The
+// smaller shapes always have one row tile.
 template <int D, int MODE, bool PF_SMALL, bool LIST>
 hipError_t launch_shape(const AttnParams& p, hipStream_t s) {
-  if (p.waves == 8 && p.ksplit == 1) return launch_one<D, 8, 1, MODE, false, LIST>(p, s);
-  if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false, LIST>(p, s);
-  return launch_one<D, 1, 1, MODE, PF_SMALL, LIST>(p, s);
+  constexpr int kStream = MODE == kModePartial ? 2 : 0;
+  if (p.waves == 8 && p.ksplit == 1) {
+    if (MODE == kModePartial && p.row_tiles == 1) return launch_one<D, 8, 1, MODE, false, LIST, kStream>(p, s);
+    return launch_one<D, 8, 1, MODE, false, LIST, 0>(p, s);
+  }
+  if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false, LIST, kStream>(p, s);
+  return launch_one<D, 1, 1, MODE, PF_SMALL, LIST, kStream>(p, s);
 }
 
 // Tile lists occur in partial launches only (sparse steps).
