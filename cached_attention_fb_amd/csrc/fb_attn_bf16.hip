@@ -545,17 +545,19 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
 // Streaming K/V: in a partial launch with one row tile per group every K/V
 // tile is read by exactly one workgroup, so its loads are marked
 // non-temporal (AUX 2); with several row tiles (frame-sized blocks) each tile
-// is re-read from L2 by every row tile and keeps the default policy.  The
-// smaller shapes always have one row tile.
+// is re-read from L2 by every row tile and keeps the default policy.
+template <int D, int MODE, bool PF_SMALL, bool LIST, int AUX>
+hipError_t launch_aux(const AttnParams& p, hipStream_t s) {
+  if (p.waves == 8 && p.ksplit == 1) return launch_one<D, 8, 1, MODE, false, LIST, AUX>(p, s);
+  if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false, LIST, AUX>(p, s);
+  return launch_one<D, 1, 1, MODE, PF_SMALL, LIST, AUX>(p, s);
+}
 template <int D, int MODE, bool PF_SMALL, bool LIST>
 hipError_t launch_shape(const AttnParams& p, hipStream_t s) {
-  constexpr int kStream = MODE == kModePartial ? 2 : 0;
-  if (p.waves == 8 && p.ksplit == 1) {
-    if (MODE == kModePartial && p.row_tiles == 1) return launch_one<D, 8, 1, MODE, false, LIST, kStream>(p, s);
-    return launch_one<D, 8, 1, MODE, false, LIST, 0>(p, s);
+  if constexpr (MODE == kModePartial) {
+    if (p.row_tiles == 1) return launch_aux<D, MODE, PF_SMALL, LIST, 2>(p, s);
   }
-  if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false, LIST, kStream>(p, s);
-  return launch_one<D, 1, 1, MODE, PF_SMALL, LIST, kStream>(p, s);
+  return launch_aux<D, MODE, PF_SMALL, LIST, 0>(p, s);
 }
 
 // Tile lists occur in partial launches only (sparse steps).
