@@ -242,12 +242,13 @@ __device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f3
   // streaming stores: the partials leave this launch for the combine, and
   // kept out of L2 they need no write-back when the launch ends
   if (hl == 0 && rl < nrows) __builtin_nontemporal_store(lse, p.part_l + split * p.part_l_stride + grow0 + rl);
-  float* od = p.part_o + split * p.part_o_stride + grow0 * D;
+  bf16* od = reinterpret_cast<bf16*>(p.part_o) + split * p.part_o_stride + grow0 * D;
 #pragma unroll
   for (int k = 0; k < 32 / kRowsPerOp; ++k) {
     const int r = k * kRowsPerOp + lane / kC, c = lane % kC;
     const f32x4 v = *reinterpret_cast<const FB_LDS f32x4*>(st + r * D + ((c ^ (r & (kC - 1))) * 4));
-    if (r < nrows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(od + (int64_t)r * D + 4 * c));
+    const bf16x4 vb = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    if (r < nrows) __builtin_nontemporal_store(vb, reinterpret_cast<bf16x4*>(od + (int64_t)r * D + 4 * c));
   }
 }
 

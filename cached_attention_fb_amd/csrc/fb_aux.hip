@@ -24,7 +24,18 @@ __device__ __forceinline__ float wave_sum(float x) {
 // and |A_old|^2 over its rows for the similarity.  In total mode (sparse attention: the
 // splits are the kept keys) the fold starts from the head's cached part and
 // the result goes to the total buffer.
-template <int D, int BATCH>
+// One float4 column of a partial A: fp32, or bf16 widened.
+template <bool PB>
+__device__ __forceinline__ f32x4 load_part(const float* base, int64_t off) {
+  if constexpr (PB) {
+    const bf16x4 t = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(base) + off);
+    return f32x4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
+  } else {
+    return *reinterpret_cast<const f32x4*>(base + off);
+  }
+}
+
+template <int D, int BATCH, bool PB>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p) {
   constexpr int kLpr = D / 4;
   constexpr int kRows = kCombineThreads / kLpr;
@@ -53,7 +64,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
   if (i < p.bs) {
     const int64_t grow = (int64_t)bh * p.bs + i;
     const float* lp = p.part_l + grow;
-    const float* ap = p.part_o + grow * D + 4 * c4;
+    const int64_t ao = grow * D + 4 * c4;   // element offset of this lane's column
     float mx = -INFINITY, wsum = 0.0f;
     f32x4 acc = {0, 0, 0, 0};
     // the cached part enters as one more term, normalised (weight 1 at its
@@ -75,7 +86,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
       for (int u = 0; u < BATCH; ++u) {
         const int si = min(s + u, splits - 1);
         l[u] = lp[si * p.part_l_stride];
-        a[u] = *reinterpret_cast<const f32x4*>(ap + si * p.part_o_stride);
+        a[u] = load_part<PB>(p.part_o, ao + si * p.part_o_stride);
         if (s + u >= splits) l[u] = -INFINITY;
       }
       // keep every load of the round ahead of the arithmetic: left to itself
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     }
     if (out_mode) {   // the block-internal part (page §2 merge), then the step's output
       const float l_in = lp[p.int_split * p.part_l_stride];
-      const f32x4 a_in = *reinterpret_cast<const f32x4*>(ap + p.int_split * p.part_o_stride);
+      const f32x4 a_in = load_part<PB>(p.part_o, ao + p.int_split * p.part_o_stride);
       const float nm = fmaxf(mx, l_in);
       if (nm > -INFINITY) {
         const float sc = fast_exp2((mx - nm) * kLog2e);
@@ -270,6 +281,9 @@ hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, h
   return dtype == FB_BF16 ? launch_attn_bf16(head_dim, mode, p, s) : launch_attn_f32(head_dim, mode, p, s);
 }
 
+template <int D, bool PB>
+hipError_t launch_combine_batch(int most, int blocks, const CombineParams& p, hipStream_t s);
+
 hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s) {
   const int blocks = p.batch * p.hq * p.row_chunks;
   if (blocks == 0) return hipSuccess;
@@ -277,15 +291,19 @@ hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s) {
   // largest split count this launch can see (the device plan's too)
   int most = p.splits;
   for (int n = 1; n <= p.dyn.groups; ++n) most = std::max(most, (int)p.dyn.splits[n]);
-  if (head_dim == 64) {
-    if (most <= 8) hipLaunchKernelGGL((combine_kernel<64, 8>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
-    else if (most <= 16) hipLaunchKernelGGL((combine_kernel<64, 16>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<64, 32>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
-  } else {
-    if (most <= 8) hipLaunchKernelGGL((combine_kernel<128, 8>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
-    else if (most <= 16) hipLaunchKernelGGL((combine_kernel<128, 16>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<128, 32>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+  if (p.part_bf16) {
+    if (head_dim == 64) return launch_combine_batch<64, true>(most, blocks, p, s);
+    return launch_combine_batch<128, true>(most, blocks, p, s);
   }
+  if (head_dim == 64) return launch_combine_batch<64, false>(most, blocks, p, s);
+  return launch_combine_batch<128, false>(most, blocks, p, s);
+}
+
+template <int D, bool PB>
+hipError_t launch_combine_batch(int most, int blocks, const CombineParams& p, hipStream_t s) {
+  if (most <= 8) hipLaunchKernelGGL((combine_kernel<D, 8, PB>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+  else if (most <= 16) hipLaunchKernelGGL((combine_kernel<D, 16, PB>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+  else hipLaunchKernelGGL((combine_kernel<D, 32, PB>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
   return hipGetLastError();
 }
 

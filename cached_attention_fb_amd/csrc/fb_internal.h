@@ -80,7 +80,9 @@ struct AttnParams {
   const void* vblk;
   int32_t int_count;
   int32_t int_split;
-  // partial epilogue: normalised A and natural-log L per split
+  // partial epilogue: normalised A and natural-log L per split.  A is bf16
+  // from the bf16 kernels (one rounding of a normalised value, 2^-9
+  // relative, on its way to the combine), fp32 from the fp32 ones.
   float* part_o;          // [splits][B][Hq][Bs][D]
   float* part_l;          // [splits][B][Hq][Bs]
   int64_t part_o_stride, part_l_stride;
@@ -95,9 +97,10 @@ struct AttnParams {
 };
 
 struct CombineParams {
-  const float* part_o;
+  const float* part_o;    // bf16 elements when part_bf16
   const float* part_l;
-  int64_t part_o_stride, part_l_stride;
+  int64_t part_o_stride, part_l_stride;   // in elements
+  int32_t part_bf16;
   int32_t splits, batch, hq, hkv, bs, row_chunks;
   HeadSel sel;
   DynPlan dyn;            // the external launch's plan (split count from the same active groups)

@@ -381,6 +381,7 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   cp.part_o = c->part_o;
   cp.part_l = c->part_l;
   cp.part_o_stride = p.part_o_stride;
+  cp.part_bf16 = c->cfg.dtype == FB_BF16 ? 1 : 0;   // the bf16 kernels hand partial A over in bf16
   cp.part_l_stride = p.part_l_stride;
   cp.splits = skip_ext ? 0 : p.splits;
   cp.batch = c->cfg.batch;

@@ -35,7 +35,9 @@
  *   - Softmax: scores are softmax_scale * <q, k>; L values are natural-log
  *     sum-exp of the scaled scores.  Attention arithmetic is fp32 with bf16
  *     operands for FB_BF16 (products exact, fp32 accumulation) and fp32
- *     operands for FB_F32.  A_out and L_out are cached in fp32 for both dtypes.
+ *     operands for FB_F32.  A_out and L_out are cached in fp32 for both dtypes;
+ *     for FB_BF16 the normalised part of each prefix chunk is rounded to bf16
+ *     once (relative 2^-9) on its way to the fp32 combine.
  *   - The library keeps no caller pointer after a call returns.  The cache is
  *     bound to the device that was current at fb_cache_alloc; calls switch to
  *     it and back.  One cache must not be used by two threads at once.
