@@ -207,3 +207,47 @@ def test_gamma_group_variant_gqa():
     assert np.max(np.abs(gpu[0].sim[fin] - ref[0].sim[fin])) <= 5e-4
     r = ref[0].reuse.reshape(ref[0].reuse.shape[0], w.batch, w.n_kv_heads, -1)
     assert np.all(r == r[..., :1])   # the heads of a group decide together
+
+
+def test_many_groups_static_plan():
+    """72 (sequence, kv head) groups, more than the device split plan covers:
+    decisions made on the device (threshold counts in device memory) then run
+    on the static grid, whose workgroups test their own group's heads; host
+    decisions on the same inputs for comparison.  D=64, GQA 2, ragged prefix."""
+    w = wl.workload("long-32k-b4").with_(batch=9, n_q_heads=16, n_kv_heads=8, head_dim=64, block=16,
+                                         steps=5, update_a=16, value_std=1.0)
+    inp = wl.generate(w, prefix=300)
+    ref = H.run_oracle(inp)
+    assert 0 < int(ref[0].reuse.sum()) < ref[0].reuse.size
+    for dc in (False, True):
+        gpu = H.run_gpu(inp, device_counts=dc)
+        errs = H.compare_block(gpu[0], ref[0], w.dtype, what=f"many groups device_counts={dc}")
+        print(f"[parity] many groups device_counts={dc} errs {errs}", flush=True)
+
+
+def test_many_groups_gamma_static_plan():
+    """GAMMA with 72 groups (static grid, per-head flags from the device);
+    threshold between two of the oracle's similarities, every decision with
+    a margin above 1e-3."""
+    import dataclasses
+    w = wl.workload("long-32k-b4").with_(batch=9, n_q_heads=16, n_kv_heads=8, head_dim=64, block=16,
+                                         steps=5, update_a=16, value_std=1.0, policy="gamma", gamma=2.0)
+    inp = wl.generate(w, prefix=300)
+    sims = np.sort(H.run_oracle(inp)[0].sim[1].ravel())
+    chosen = None
+    for _, i in sorted(((sims[i + 1] - sims[i], i) for i in range(len(sims) // 4, 3 * len(sims) // 4)),
+                       reverse=True):
+        trial = dataclasses.replace(inp, workload=w.with_(gamma=float(0.5 * (sims[i] + sims[i + 1]))))
+        ref = H.run_oracle(trial)
+        defined = ref[0].sim[~np.isnan(ref[0].sim)]
+        if np.min(np.abs(defined - trial.workload.gamma)) > 1e-3:
+            chosen = (trial, ref)
+            break
+    assert chosen is not None
+    trial, ref = chosen
+    gpu = H.run_gpu(trial)
+    errs = H.compare_block(gpu[0], ref[0], w.dtype, what="many groups gamma")
+    fin = ~np.isnan(ref[0].sim)
+    assert np.max(np.abs(gpu[0].sim[fin] - ref[0].sim[fin])) <= 5e-4
+    assert 0 < int(ref[0].reuse.sum()) < ref[0].reuse[2:].size
+    print(f"[parity] many groups gamma {trial.workload.gamma:.6f} errs {errs}", flush=True)
