@@ -298,15 +298,27 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   // system while the first is awaited), all three through the LDS DMA path.
   // Q goes through LDS rather than straight into registers because the
   // compiler cannot order register loads against the DMA loads and would
-  // drain the whole ring before every MFMA that reads Q.
+  // drain the whole ring before every MFMA that reads Q (except in the
+  // lone-wave merge launch, see below).
   ExtPart<D> ext;
   const bool ext_lane = MODE == kModeMerge && row_ok && kh == 0;
   if (ext_lane) {
     ext.load_state(p, bh);
     if constexpr (PREFETCH_EXT) ext.load_data(p, grow, hl);   // in flight with Q and the tiles
   }
+  // The lone-wave merge launch (short blocks: one tile) loads Q straight into
+  // registers, in flight with everything else; it waits for all loads before
+  // its first tile anyway.
+  constexpr bool kQReg = MODE == kModeMerge && ROWW == 1 && PREFETCH_EXT;
+  bf16x8 qf[D / 16];
   FB_LDS char* q_lds = lds + P::q_offset(P::ring_stages(p.ring_keys)) + rw * 32 * D * 2;
-  if (kh == 0 && wave_live) issue_q<D>(q_lds, qg + (grow - rl) * D, p.rows - row0, lane);
+  if constexpr (kQReg) {
+    const bf16* qrow = qg + (grow - rl + min(rl, p.rows - row0 - 1)) * D + 8 * hl;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) qf[t] = *reinterpret_cast<const bf16x8*>(qrow + 16 * t);
+  } else {
+    if (kh == 0 && wave_live) issue_q<D>(q_lds, qg + (grow - rl) * D, p.rows - row0, lane);
+  }
   int issued;
   if (ntiles >= 2) {
     issue_tile<D, WAVES, kAux>(lds, kb, vb, tm.key0(0), lim, wave, lane);
@@ -323,8 +335,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   }
   __builtin_amdgcn_s_barrier();   // every wave's share of tile 0 (and Q) landed
   // Q^T as the B operand: lane (row, hl) holds Q[row][16t + 8hl .. +7].
-  bf16x8 qf[D / 16];
-  {
+  if constexpr (!kQReg) {
     uint32_t qa[D / 16];
     const uint32_t q0 = (uint32_t)(uintptr_t)q_lds;
 #pragma unroll
