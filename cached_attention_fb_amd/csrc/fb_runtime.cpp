@@ -203,6 +203,7 @@ int choose_splits(fb_cache* c, int n_keys, int active_groups, int co_items = 0, 
     want = std::max(1, std::min({want, tiles, c->splits_cap}));
     const int tiles_per = (tiles + want - 1) / want;
     const int sp = (tiles + tiles_per - 1) / tiles_per;   // no empty chunk
+    if (c->split_memo.size() >= 4096) c->split_memo.clear();   // bounded: prefixes grow block by block
     c->split_memo[key] = sp;
     return sp;
   }
