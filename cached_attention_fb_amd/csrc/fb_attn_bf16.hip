@@ -83,6 +83,56 @@ __device__ __forceinline__ void tr_read_half(u32x2 (&r)[D / 8], const uint32_t (
   }
 }
 
+// Both 32-key halves' V^T operands in one asm block and one LDS wait (the
+// 8-row-wave shape, where each wave takes whole tiles): r0 = half 0, r1 =
+// half 1, each in the layout of tr_read_half.  One exposed LDS latency per
+// tile instead of two.
+template <int D>
+__device__ __forceinline__ void tr_read_both(u32x2 (&r0)[D / 8], u32x2 (&r1)[D / 8], const uint32_t (&base)[D / 32]) {
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %32 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %32 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %2, %33 offset:0\n\t"
+        "ds_read_b64_tr_b16 %3, %33 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %4, %34 offset:0\n\t"
+        "ds_read_b64_tr_b16 %5, %34 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %35 offset:0\n\t"
+        "ds_read_b64_tr_b16 %7, %35 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %8, %32 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %9, %32 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %10, %33 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %11, %33 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %12, %34 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %13, %34 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %14, %35 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %15, %35 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %16, %32 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %17, %32 offset:10240\n\t"
+        "ds_read_b64_tr_b16 %18, %33 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %19, %33 offset:10240\n\t"
+        "ds_read_b64_tr_b16 %20, %34 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %21, %34 offset:10240\n\t"
+        "ds_read_b64_tr_b16 %22, %35 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %23, %35 offset:10240\n\t"
+        "ds_read_b64_tr_b16 %24, %32 offset:12288\n\t"
+        "ds_read_b64_tr_b16 %25, %32 offset:14336\n\t"
+        "ds_read_b64_tr_b16 %26, %33 offset:12288\n\t"
+        "ds_read_b64_tr_b16 %27, %33 offset:14336\n\t"
+        "ds_read_b64_tr_b16 %28, %34 offset:12288\n\t"
+        "ds_read_b64_tr_b16 %29, %34 offset:14336\n\t"
+        "ds_read_b64_tr_b16 %30, %35 offset:12288\n\t"
+        "ds_read_b64_tr_b16 %31, %35 offset:14336\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0[0]), "=&v"(r0[1]), "=&v"(r0[2]), "=&v"(r0[3]), "=&v"(r0[4]), "=&v"(r0[5]), "=&v"(r0[6]), "=&v"(r0[7]), "=&v"(r0[8]), "=&v"(r0[9]), "=&v"(r0[10]), "=&v"(r0[11]), "=&v"(r0[12]), "=&v"(r0[13]), "=&v"(r0[14]), "=&v"(r0[15]), "=&v"(r1[0]), "=&v"(r1[1]), "=&v"(r1[2]), "=&v"(r1[3]), "=&v"(r1[4]), "=&v"(r1[5]), "=&v"(r1[6]), "=&v"(r1[7]), "=&v"(r1[8]), "=&v"(r1[9]), "=&v"(r1[10]), "=&v"(r1[11]), "=&v"(r1[12]), "=&v"(r1[13]), "=&v"(r1[14]), "=&v"(r1[15])
+        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3])
+        : "memory");
+  } else {
+    tr_read_half<D, 0>(r0, base);
+    tr_read_half<D, 1>(r1, base);
+  }
+}
+
 // Wait until at most `after` tiles' DMA loads (kLpt per tile and wave) are
 // still in flight, i.e. this wave's share of the current tile has landed.
 // When after*kLpt does not fit the 6-bit counter, wait for fewer (safe).
@@ -131,6 +181,40 @@ __device__ __forceinline__ void k_read_half(u32x4 (&r)[D / 16], const uint32_t (
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
         : "memory");
+  }
+}
+
+// Both halves' K^T operand fragments in one asm block and one LDS wait
+// (r0 = keys 0-31 of the tile, r1 = keys 32-63), as k_read_half.
+template <int D>
+__device__ __forceinline__ void k_read_both(u32x4 (&r0)[D / 16], u32x4 (&r1)[D / 16], const uint32_t (&a)[D / 16]) {
+  if constexpr (D == 128) {
+    constexpr int H = 32 * D * 2;
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %17\n\t"
+        "ds_read_b128 %2, %18\n\t"
+        "ds_read_b128 %3, %19\n\t"
+        "ds_read_b128 %4, %20\n\t"
+        "ds_read_b128 %5, %21\n\t"
+        "ds_read_b128 %6, %22\n\t"
+        "ds_read_b128 %7, %23\n\t"
+        "ds_read_b128 %8, %16 offset:%24\n\t"
+        "ds_read_b128 %9, %17 offset:%24\n\t"
+        "ds_read_b128 %10, %18 offset:%24\n\t"
+        "ds_read_b128 %11, %19 offset:%24\n\t"
+        "ds_read_b128 %12, %20 offset:%24\n\t"
+        "ds_read_b128 %13, %21 offset:%24\n\t"
+        "ds_read_b128 %14, %22 offset:%24\n\t"
+        "ds_read_b128 %15, %23 offset:%24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0[0]), "=&v"(r0[1]), "=&v"(r0[2]), "=&v"(r0[3]), "=&v"(r0[4]), "=&v"(r0[5]), "=&v"(r0[6]), "=&v"(r0[7]),
+          "=&v"(r1[0]), "=&v"(r1[1]), "=&v"(r1[2]), "=&v"(r1[3]), "=&v"(r1[4]), "=&v"(r1[5]), "=&v"(r1[6]), "=&v"(r1[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(H)
+        : "memory");
+  } else {
+    k_read_half<D, 0>(r0, a);
+    k_read_half<D, 32 * D * 2>(r1, a);
   }
 }
 
@@ -395,6 +479,19 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
       for (int t = 0; t < D / 16; ++t) ka[t] = ks_off + k_off[t];
       f32x16 s[NH];
       const int nh_live = (kShortSkip && tile0 + 32 >= lim) ? 1 : NH;
+      if constexpr (NH == 2 && ROWW > 1) {
+        // both halves' K fragments in one batched read (one LDS wait per
+        // tile), then the two independent S chains interleaved
+        u32x4 kf0[D / 16], kf1[D / 16];
+        k_read_both<D>(kf0, kf1, ka);
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf0[t]), qf[t], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf1[t]), qf[t], s[1], 0, 0, 0);
+        }
+      } else {
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         s[h] = f32x16{};
@@ -405,6 +502,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
           s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[h], 0, 0, 0);
+      }
       }
       // Ragged last tile: keys at or past the limit do not count.
       const int key0 = tile0 + 32 * kh * NH;
@@ -442,12 +540,26 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) vbase[dt] = vs_off + tr_off[dt];
       u32x2 vr[D / 8];
+      u32x2 vr1[D / 8];
       bf16x8 pb0[2];
-      if (kh * NH == 0) tr_read_half<D, 0>(vr, vbase);
+      if constexpr (NH == 2 && ROWW > 1) tr_read_both<D>(vr, vr1, vbase);
+      else if (kh * NH == 0) tr_read_half<D, 0>(vr, vbase);
       else tr_read_half<D, 1>(vr, vbase);
       exp_half(s[0], mref, p.scale_log2, lsum, pb0);
       if (kShortSkip && nh_live == 1) {
         pv_half<kDt>(o, vr, pb0);   // the second half holds no key (short block)
+      } else if constexpr (NH == 2 && ROWW > 1) {
+        // half 1's V^T was read with half 0's (one LDS wait); its
+        // exponentials are interleaved with half 0's PV MFMAs
+        bf16x8 pb1[2];
+        pv_half<kDt>(o, vr, pb0);
+        exp_half(s[NH - 1], mref, p.scale_log2, lsum, pb1);
+#pragma unroll
+        for (int i = 0; i < 2 * kDt; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // then VALU
+        }
+        pv_half<kDt>(o, vr1, pb1);
       } else if constexpr (NH == 2) {
         // half 1's exponentials are interleaved with half 0's PV MFMAs
         bf16x8 pb1[2];
