@@ -504,11 +504,22 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
           s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[h], 0, 0, 0);
       }
       }
-      // Ragged last tile: keys at or past the limit do not count.
+      // Ragged last tile: keys at or past the limit do not count.  In the
+      // single-wave kernels (short blocks: often one tile, often half full) a
+      // half with no key is filled whole and a full half left alone; the
+      // multi-wave loops keep the plain form, whose code schedules better.
       const int key0 = tile0 + 32 * kh * NH;
       if (key0 + 32 * NH > lim) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
+          if constexpr (kShortSkip) {
+            if (key0 + 32 * h + 32 <= lim) continue;
+            if (key0 + 32 * h >= lim) {
+#pragma unroll
+              for (int j = 0; j < 16; ++j) s[h][j] = -INFINITY;
+              continue;
+            }
+          }
 #pragma unroll
           for (int j = 0; j < 16; ++j)
             if (key0 + 32 * h + 8 * (j >> 2) + 4 * hl + (j & 3) >= lim) s[h][j] = -INFINITY;
@@ -526,7 +537,9 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
         }
         mx = pair_max(mx) * p.scale_log2;
         const bool raise = mx > m + kRescale;
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        if (kShortSkip && t_i == 0) {
+          m = raise ? mx : m;   // first tile: O and the sum are still zero, nothing to rescale
+        } else if (__builtin_amdgcn_ballot_w64(raise) != 0) {
           const float m_new = raise ? mx : m;
           const float alpha = fast_exp2(m - m_new);
           m = m_new;
@@ -634,9 +647,11 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   const float ltot = pair_sum(lsum);
   if (!row_ok) return;
   {
-    if (p.reuse_rec != nullptr && hl == 0 && (row % p.bs) == 0) p.reuse_rec[bh] = head_selected(p.sel, b, bh) ? 0 : 1;
     if constexpr (!PREFETCH_EXT) ext.load_data(p, grow, hl);
     merge_store<bf16, D>(p, o, m, ltot, ext, grow, hl);
+    // The decision record goes last: a store issued before the merge would
+    // hold up its wait for the cached part's loads (one counter for both).
+    if (p.reuse_rec != nullptr && hl == 0 && (row % p.bs) == 0) p.reuse_rec[bh] = head_selected(p.sel, b, bh) ? 0 : 1;
   }
 }
 

@@ -110,10 +110,12 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
     store_partial<D>(p, o, m, ltot, it.split, grow, hl);
   } else {
     const int bh = b * p.hq + g * grp + row / p.bs;
-    if (p.reuse_rec != nullptr && hl == 0 && (row % p.bs) == 0) p.reuse_rec[bh] = head_selected(p.sel, b, bh) ? 0 : 1;
     ExtPart<D> ext;
     ext.load(p, bh, grow, hl);
     merge_store<float, D>(p, o, m, ltot, ext, grow, hl);
+    // the decision record last, so that the merge's wait for the cached
+    // part's loads does not also wait for this store
+    if (p.reuse_rec != nullptr && hl == 0 && (row % p.bs) == 0) p.reuse_rec[bh] = head_selected(p.sel, b, bh) ? 0 : 1;
   }
 }
 
