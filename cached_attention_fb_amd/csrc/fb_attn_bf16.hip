@@ -340,8 +340,10 @@ __device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f3
 template <int D, int ROWW>
 constexpr int xch_bytes() { return ROWW * (16 * (D / 32) + 2) * 64 * 4; }
 
-// AUX: cache policy of the K/V DMA loads (see issue_tile).
-template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT, bool LIST, int AUX>
+// AUX: cache policy of the K/V DMA loads (see issue_tile).  ONE: the launch
+// gives every item at most one key tile (short blocks), so the loop body runs
+// once at most and carries no refill.
+template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT, bool LIST, int AUX, bool ONE>
 __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const AttnParams p) {
   constexpr int WAVES = ROWW * KSPLIT;
   constexpr int NH = 2 / KSPLIT;   // 32-key halves of a tile per wave
@@ -360,7 +362,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
   const int b = it.b, g = it.g, grp = p.hq / p.hkv;
   const int key_begin = it.key_begin, key_end = it.key_end;
-  const int ntiles = key_end > key_begin ? (key_end - key_begin + kKeyTile - 1) / kKeyTile : 0;
+  const int ntiles_all = key_end > key_begin ? (key_end - key_begin + kKeyTile - 1) / kKeyTile : 0;
+  const int ntiles = ONE ? min(ntiles_all, 1) : ntiles_all;
   const int row0 = it.rt * ROWW * 32 + rw * 32;
   const int row = row0 + rl;
   const bool row_ok = row < p.rows;
@@ -591,9 +594,11 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     }
     // Refill after the compute, so that a stalled issue does not delay it:
     // the stage of tile t_i-1 is free (every wave passed the barrier above).
-    for (; issued < ntiles && issued <= t_i + P::kStages - 1; ++issued)
-      issue_tile<D, WAVES, kAux>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, tm.key0(issued), lim, wave,
-                           lane);
+    if constexpr (!ONE) {
+      for (; issued < ntiles && issued <= t_i + P::kStages - 1; ++issued)
+        issue_tile<D, WAVES, kAux>(lds + (issued % P::kStages) * P::kStageBytes, kb, vb, tm.key0(issued), lim, wave,
+                                   lane);
+    }
   }
 
   if constexpr (KSPLIT == 2) {
@@ -655,7 +660,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   }
 }
 
-template <int D, int ROWW, int KSPLIT, int MODE, bool PF, bool LIST, int AUX>
+template <int D, int ROWW, int KSPLIT, int MODE, bool PF, bool LIST, int AUX, bool ONE = false>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   using P = Pipe<D, ROWW * KSPLIT>;
   const int blocks = p.grid > 0 ? p.grid : p.batch * p.hkv * p.splits * p.row_tiles;
@@ -666,7 +671,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
                                     KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX, ONE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -676,7 +681,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   int lds = std::max(ring * P::kStageBytes, P::q_offset(ring) + kQBytes);
   if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
   lds = std::max(lds, kStageOut);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX>), dim3(blocks), dim3(64 * ROWW * KSPLIT),
+  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX, ONE>), dim3(blocks), dim3(64 * ROWW * KSPLIT),
                      lds, s, p);
   return hipGetLastError();
 }
@@ -689,6 +694,8 @@ template <int D, int MODE, bool PF_SMALL, bool LIST, int AUX>
 hipError_t launch_aux(const AttnParams& p, hipStream_t s) {
   if (p.waves == 8 && p.ksplit == 1) return launch_one<D, 8, 1, MODE, false, LIST, AUX>(p, s);
   if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false, LIST, AUX>(p, s);
+  // block-internal attention of a block of at most one key tile
+  if (MODE == kModeMerge && p.ring_keys <= kKeyTile) return launch_one<D, 1, 1, MODE, PF_SMALL, LIST, AUX, true>(p, s);
   return launch_one<D, 1, 1, MODE, PF_SMALL, LIST, AUX>(p, s);
 }
 template <int D, int MODE, bool PF_SMALL, bool LIST>
