@@ -360,7 +360,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   const AttnItem it = attn_item(p, MODE == kModePartial);
   if constexpr (MODE == kModePartial) record_decisions(p);
   if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
-  const int b = it.b, g = it.g, grp = p.hq / p.hkv;
+  const int b = it.b, g = it.g, grp = p.grp;
   const int key_begin = it.key_begin, key_end = it.key_end;
   const int ntiles_all = key_end > key_begin ? (key_end - key_begin + kKeyTile - 1) / kKeyTile : 0;
   const int ntiles = ONE ? min(ntiles_all, 1) : ntiles_all;

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnParams p) 
   const AttnItem it = attn_item(p, MODE == kModePartial);
   if constexpr (MODE == kModePartial) record_decisions(p);
   if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
-  const int b = it.b, g = it.g, grp = p.hq / p.hkv;
+  const int b = it.b, g = it.g, grp = p.grp;
   const int key_begin = it.key_begin, key_end = it.key_end;
   const int row0 = it.rt * kF32Waves * 32 + wave * 32;
   const int row = row0 + rl;

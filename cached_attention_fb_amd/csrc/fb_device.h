@@ -156,13 +156,17 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
     int w = xcd_remap(w0, (int)gridDim.x - int_count);
     it.rt = w % p.row_tiles;
     w /= p.row_tiles;
-    it.split = w % p.splits;
-    w /= p.splits;
+    if (partial) {
+      it.split = w % p.splits;
+      w /= p.splits;
+    } else {
+      it.split = 0;   // merge launches run one key range per group
+    }
     it.g = w % p.hkv;
     it.b = w / p.hkv;
     it.ok = true;
     if (partial) {
-      const int grp = p.hq / p.hkv;
+      const int grp = p.grp;
       bool any = false;
       for (int i = 0; i < grp; ++i) any |= head_selected(p.sel, it.b, it.b * p.hq + it.g * grp + i);
       it.ok = any;

@@ -62,6 +62,7 @@ struct AttnParams {
   int32_t tiles_stride;
   int32_t n_phys;
   int32_t batch, hq, hkv, bs, rows;   // rows = (Hq/Hkv) * Bs
+  int32_t grp;            // Hq / Hkv (query heads per kv head)
   int32_t waves;          // wave64 per workgroup
   int32_t ksplit;         // 1, or 2: two wave sets split every key tile (waves/ksplit own 32 rows each)
   int32_t row_tiles;      // ceil(rows / (32 * waves / ksplit))

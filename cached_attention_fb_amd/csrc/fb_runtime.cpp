@@ -284,6 +284,7 @@ fbk::AttnParams attn_common(const fb_cache* c, const void* q, int waves, int ksp
   p.hkv = c->cfg.n_kv_heads;
   p.bs = c->cfg.block_size;
   p.rows = c->rows;
+  p.grp = c->group;
   p.scale_log2 = c->scale * 1.4426950408889634f;
   p.int_count = 0;   // no block-internal items unless a fused step adds them
   return p;
