@@ -357,7 +357,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rw = wave % ROWW, kh = wave / ROWW;
   const int rl = lane & 31, hl = lane >> 5;
-  const AttnItem it = attn_item(p, MODE == kModePartial);
+  // ONE: a 3-D grid (row tile, kv head, sequence), one key range per group
+  const AttnItem it = ONE ? grid_item(p) : attn_item(p, MODE == kModePartial);
   if constexpr (MODE == kModePartial) record_decisions(p);
   if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
   const int b = it.b, g = it.g, grp = p.grp;
@@ -665,6 +666,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   using P = Pipe<D, ROWW * KSPLIT>;
   const int blocks = p.grid > 0 ? p.grid : p.batch * p.hkv * p.splits * p.row_tiles;
   if (blocks == 0) return hipSuccess;
+  const dim3 grid = ONE ? dim3(p.row_tiles, p.hkv, p.batch) : dim3(blocks);
   constexpr int kStageOut = MODE == kModePartial ? ROWW * 32 * D * 4 : 0;   // partial staging (KSPLIT 1)
   constexpr int kQBytes = ROWW * 32 * D * 2;
   constexpr int kMaxLds = std::max({P::kLdsBytes, (P::kStages - 1) * P::kStageBytes + kQBytes,
@@ -681,7 +683,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   int lds = std::max(ring * P::kStageBytes, P::q_offset(ring) + kQBytes);
   if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
   lds = std::max(lds, kStageOut);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX, ONE>), dim3(blocks), dim3(64 * ROWW * KSPLIT),
+  hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX, ONE>), grid, dim3(64 * ROWW * KSPLIT),
                      lds, s, p);
   return hipGetLastError();
 }

@@ -177,6 +177,21 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
   return it;
 }
 
+// Work item of a merge launch on a 3-D grid (x: row tile, y: kv head, z:
+// sequence): one key range, the whole of the block's keys; no division.
+__device__ __forceinline__ AttnItem grid_item(const AttnParams& p) {
+  AttnItem it;
+  it.internal = false;
+  it.rt = blockIdx.x;
+  it.g = blockIdx.y;
+  it.b = blockIdx.z;
+  it.split = 0;
+  it.key_begin = 0;
+  it.key_end = p.n_keys;
+  it.ok = true;
+  return it;
+}
+
 // Key tiles of a work item.  Contiguous range: tile v starts at key
 // key_begin + 64v and keys at or past key_end (the range's end) hold no key.
 // Tile list: tile v starts at key 64 * list[v] (the item's part of its group's
