@@ -261,10 +261,14 @@ struct Pipe {
     const int t = (keys_per_split + kKeyTile - 1) / kKeyTile;
     return t < 1 ? 1 : (t < kStages ? t : kStages);
   }
-  // Q staging (ROWW x 32 rows x D, read once before the first tile): in ring
-  // stages 2-3 when the ring is full (those are first filled after Q has
-  // been read), else past the ring.
-  __host__ __device__ static int q_offset(int ring) { return ring == kStages ? 2 * kStageBytes : ring * kStageBytes; }
+  // Q staging (ROWW x 32 rows x D, read once before the first tile): past
+  // the ring when a full ring and Q fit the CU's 160 KB (no barrier between
+  // reading Q and refilling the ring), else, with a full ring, in stages 2-3
+  // (first filled after Q has been read).
+  __host__ __device__ static constexpr bool q_past(int rows_w) { return kLdsBytes + rows_w * 32 * D * 2 <= 160 * 1024; }
+  __host__ __device__ static constexpr int q_offset(int ring, int rows_w) {
+    return (ring == kStages && !q_past(rows_w)) ? 2 * kStageBytes : ring * kStageBytes;
+  }
 };
 
 // AUX: cache policy of the DMA loads (2: non-temporal, for K/V that no other
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   // its first tile anyway.
   constexpr bool kQReg = MODE == kModeMerge && ROWW == 1 && PREFETCH_EXT;
   bf16x8 qf[D / 16];
-  FB_LDS char* q_lds = lds + P::q_offset(P::ring_stages(p.ring_keys)) + rw * 32 * D * 2;
+  FB_LDS char* q_lds = lds + P::q_offset(P::ring_stages(p.ring_keys), ROWW) + rw * 32 * D * 2;
   if constexpr (kQReg) {
     const bf16* qrow = qg + (grow - rl + min(rl, p.rows - row0 - 1)) * D + 8 * hl;
 #pragma unroll
@@ -434,8 +438,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     for (int t = 0; t < D / 16; ++t) qf[t] = __builtin_bit_cast(bf16x8, qr[t]);
   }
   // When Q sits in ring stages 2-3, every wave must have read it before the
-  // first refill writes there.
-  if (P::ring_stages(p.ring_keys) == P::kStages) __builtin_amdgcn_s_barrier();
+  // first refill writes there (past the ring it needs no barrier).
+  if (!P::q_past(ROWW) && P::ring_stages(p.ring_keys) == P::kStages) __builtin_amdgcn_s_barrier();
 
   f32x16 o[kDt];
 #pragma unroll
@@ -669,7 +673,8 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   const dim3 grid = ONE ? dim3(p.row_tiles, p.hkv, p.batch) : dim3(blocks);
   constexpr int kStageOut = MODE == kModePartial ? ROWW * 32 * D * 4 : 0;   // partial staging (KSPLIT 1)
   constexpr int kQBytes = ROWW * 32 * D * 2;
-  constexpr int kMaxLds = std::max({P::kLdsBytes, (P::kStages - 1) * P::kStageBytes + kQBytes,
+  constexpr int kMaxLds = std::max({P::kLdsBytes, P::q_offset(P::kStages, ROWW) + kQBytes,
+                                    (P::kStages - 1) * P::kStageBytes + kQBytes,
                                     KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
   static bool attr_set = false;
   if (!attr_set) {
@@ -680,7 +685,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   }
   // a workgroup never uses more ring stages than its key range has tiles
   const int ring = P::ring_stages(p.ring_keys);
-  int lds = std::max(ring * P::kStageBytes, P::q_offset(ring) + kQBytes);
+  int lds = std::max(ring * P::kStageBytes, P::q_offset(ring, ROWW) + kQBytes);
   if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
   lds = std::max(lds, kStageOut);
   hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX, ONE>), grid, dim3(64 * ROWW * KSPLIT),

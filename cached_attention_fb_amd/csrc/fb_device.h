@@ -166,9 +166,15 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
     it.b = w / p.hkv;
     it.ok = true;
     if (partial) {
-      const int grp = p.grp;
-      bool any = false;
-      for (int i = 0; i < grp; ++i) any |= head_selected(p.sel, it.b, it.b * p.hq + it.g * grp + i);
+      bool any;
+      if (p.sel.m == nullptr && p.sel.flags == nullptr) {
+        // decided per sequence (the host's threshold decisions): no head loop
+        any = p.sel.every_seq || ((p.sel.seq_bits[it.b >> 5] >> (it.b & 31)) & 1u);
+      } else {
+        const int grp = p.grp;
+        any = false;
+        for (int i = 0; i < grp; ++i) any |= head_selected(p.sel, it.b, it.b * p.hq + it.g * grp + i);
+      }
       it.ok = any;
     }
   }
