@@ -340,9 +340,10 @@ __device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f3
   }
 }
 
-// LDS bytes of the end-of-loop exchange between the two key halves.
+// LDS bytes of the end-of-loop exchange between the two key halves: per row
+// wave, 4 D/32 + 1 chunks of 16 bytes per lane (O, then m and the sum).
 template <int D, int ROWW>
-constexpr int xch_bytes() { return ROWW * (16 * (D / 32) + 2) * 64 * 4; }
+constexpr int xch_bytes() { return ROWW * (4 * (D / 32) + 1) * 64 * 16; }
 
 // AUX: cache policy of the K/V DMA loads (see issue_tile).  ONE: the launch
 // gives every item at most one key tile (short blocks), so the loop body runs
@@ -608,31 +609,37 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
 
   if constexpr (KSPLIT == 2) {
     // Merge the two key halves of each row: the second wave set hands its
-    // (O, m, lane sum) to the first through LDS.  No DMA is in flight here
+    // (O, m, lane sum) to the first through LDS, 16 bytes per lane and
+    // instruction (chunk c of lane l at c*64 + l).  No DMA is in flight here
     // (the last tile waited for vmcnt 0), so the ring can be reused.
-    constexpr int kRegs = 16 * kDt + 2;
-    FB_LDS float* xch = (FB_LDS float*)lds + rw * kRegs * 64 + lane;
+    constexpr int kChunks = 4 * kDt + 1;
+    FB_LDS f32x4* xch = (FB_LDS f32x4*)lds + rw * kChunks * 64 + lane;
     __builtin_amdgcn_s_barrier();
     if (kh == 1 && wave_live) {
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) xch[(dt * 16 + j) * 64] = o[dt][j];
+        for (int q = 0; q < 4; ++q)
+          xch[(4 * dt + q) * 64] = f32x4{o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]};
       }
-      xch[(16 * kDt) * 64] = m;
-      xch[(16 * kDt + 1) * 64] = lsum;
+      xch[(4 * kDt) * 64] = f32x4{m, lsum, 0.0f, 0.0f};
     }
     __builtin_amdgcn_s_barrier();
     if (kh == 1) return;
     if (wave_live) {
-      const float m2 = xch[(16 * kDt) * 64], l2 = xch[(16 * kDt + 1) * 64];
+      const f32x4 ml = xch[(4 * kDt) * 64];
+      const float m2 = ml[0], l2 = ml[1];
       const float mt = fmaxf(m, m2);
       const float a1 = m > -INFINITY ? fast_exp2(m - mt) : 0.0f;
       const float a2 = m2 > -INFINITY ? fast_exp2(m2 - mt) : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[dt][j] = a1 * o[dt][j] + a2 * xch[(dt * 16 + j) * 64];
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = xch[(4 * dt + q) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[dt][4 * q + e] = a1 * o[dt][4 * q + e] + a2 * v[e];
+        }
       }
       lsum = a1 * lsum + a2 * l2;
       m = mt;
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     if constexpr (KSPLIT == 1) __builtin_amdgcn_s_barrier();   // every wave finished reading the ring
     if (!wave_live) return;
     const float ltot = pair_sum(lsum);
-    constexpr int kRegionFloats = KSPLIT == 2 ? (16 * kDt + 2) * 64 : 32 * D;
+    constexpr int kRegionFloats = KSPLIT == 2 ? (4 * kDt + 1) * 64 * 4 : 32 * D;
     store_partial_rows<D>(p, o, m, ltot, it.split, grow - rl, min(32, p.rows - row0),
                           (FB_LDS float*)lds + rw * kRegionFloats, lane);
     return;
