@@ -708,6 +708,7 @@ template <int D, int MODE, bool PF_SMALL, bool LIST, int AUX>
 hipError_t launch_aux(const AttnParams& p, hipStream_t s) {
   if (p.waves == 8 && p.ksplit == 1) return launch_one<D, 8, 1, MODE, false, LIST, AUX>(p, s);
   if (p.waves == 8 && p.ksplit == 2) return launch_one<D, 4, 2, MODE, false, LIST, AUX>(p, s);
+  if (p.waves == 4 && p.ksplit == 1) return launch_one<D, 4, 1, MODE, false, LIST, AUX>(p, s);
   // block-internal attention of a block of at most one key tile
   if (MODE == kModeMerge && p.ring_keys <= kKeyTile) return launch_one<D, 1, 1, MODE, PF_SMALL, LIST, AUX, true>(p, s);
   return launch_one<D, 1, 1, MODE, PF_SMALL, LIST, AUX>(p, s);

@@ -252,6 +252,7 @@ fbk::HeadSel all_heads(const fb_cache* c) {
 // split count the host would choose for n groups (makespan rule).  The
 // scratch allows at most max(static choice, kDynSplitCap) splits.
 constexpr int kDynSplitCap = 16;
+constexpr int kShortItemKeys = 6 * fbk::kKeyTile;   // work items up to this many keys: the one-wave-per-SIMD shape
 bool dyn_possible(const fb_cache* c) { return c->cfg.batch * c->cfg.n_kv_heads <= fbk::kDynMaxGroups; }
 void plan_dyn(fb_cache* c, int n_keys, int co_items = 0, int co_tiles = 0) {
   if (c->dyn_keys == n_keys && c->dyn_co == co_items) return;
@@ -363,6 +364,16 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
     p.int_split = c->splits_cap;
     p.grid = ext_items + p.int_count;
     p.ring_keys = std::max(p.ring_keys, ((c->cfg.block_size + fbk::kKeyTile - 1) / fbk::kKeyTile) * fbk::kKeyTile);
+  }
+  // Short work items (few tiles each, as at dLLM prefix lengths) run one
+  // wave per SIMD over whole tiles instead of two waves on the key halves:
+  // a short loop cannot hide the key-half exchange and its barrier, a long
+  // one gains from the second wave (measured crossover 6-8 tiles per item).
+  // The rows per workgroup, hence the row tiles and the split plan, are the
+  // same for both shapes.
+  if (p.ksplit == 2 && p.ring_keys <= kShortItemKeys) {
+    p.waves = 4;
+    p.ksplit = 1;
   }
   p.sel = sel;
   p.reuse_rec = o.rec;

@@ -80,7 +80,9 @@ CASES = [
     Case("bf16", 128, 32, 8, 32, 4000, std=1.0, splits=7),
     Case("f32", 64, 4, 4, 32, 512, splits=3),
     Case("bf16", 128, 12, 12, 300, 2000, splits=2),
-    Case("bf16", 64, 8, 2, 32, 1000),        # D=64 in the 4x2 shape (128 packed rows)
+    Case("bf16", 64, 8, 2, 32, 1000),        # D=64, 128 packed rows, short items: one wave per SIMD
+    Case("bf16", 64, 8, 2, 32, 1000, splits=2),   # D=64, 128 packed rows, 8-tile items: the 4x2 shape
+    Case("bf16", 128, 8, 2, 32, 300),        # 128 rows, short items with a ragged last tile
     Case("bf16", 64, 4, 4, 16, 700),         # D=64 in the one-wave shape
     Case("bf16", 64, 4, 1, 200, 900),        # D=64, 8-row-wave shape, 4 row tiles
     Case("bf16", 128, 16, 2, 40, 2000),      # GQA 8, 2 row tiles

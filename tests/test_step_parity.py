@@ -50,6 +50,13 @@ def test_dllm_unscaled_stress():
     _full_check(wl.workload("dllm-8k").with_(value_std=1.0, steps=4), prefix=3000)
 
 
+def test_dllm_long_items_key_half_shape():
+    """Two splits of a 3000-key prefix: 24-tile items run on the key-half
+    (4x2) shape, block-internal items in the same launch; the default plan
+    at these shapes gives short items on one wave per SIMD."""
+    _full_check(wl.workload("dllm-8k").with_(steps=4), prefix=3000, kv_splits=2)
+
+
 def test_long_batch4_small_prefix():
     _full_check(wl.workload("long-32k-b4").with_(steps=6), prefix=700)
 
