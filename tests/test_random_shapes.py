@@ -69,3 +69,35 @@ def test_draws_cover_the_shapes():
         seen.add(("empty", prefix == 0))
     for key in [("rows", k) for k in range(4)] + [("one_tile", True), ("one_tile", False), ("d", 64), ("d", 128)]:
         assert key in seen, key
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(0, N_CASES, 3))
+def test_random_shape_device_counts(i):
+    """The same shapes with the threshold counts in device memory: decisions
+    made by the kernels, compared with the oracle's."""
+    w, prefix, splits = draw(i)
+    print(f"[random-dev {i}] {w.dtype} B={w.batch} Hq/Hkv={w.n_q_heads}/{w.n_kv_heads} D={w.head_dim} "
+          f"Bs={w.block} prefix={prefix} splits={splits}", flush=True)
+    inp = wl.generate(w, prefix=prefix)
+    gpu = H.run_gpu(inp, kv_splits=splits, device_counts=True)
+    ref = H.run_oracle(inp)
+    for b, (g, r) in enumerate(zip(gpu, ref)):
+        H.compare_block(g, r, w.dtype, what=f"random-dev {i} block {b}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", [i for i in range(1, N_CASES, 2) if i % 8 != 7])
+def test_random_shape_sparse(i):
+    """The bf16 shapes through fb_step_sparse with a seeded selection of
+    20-60 % of the prefix tiles (tile-list attention in every launch shape)."""
+    from test_sparse_parity import run_gpu_sparse, run_oracle_sparse
+    w, prefix, _ = draw(i)
+    density = 0.2 + 0.4 * ((i * 37) % 11) / 10
+    print(f"[random-sparse {i}] B={w.batch} Hq/Hkv={w.n_q_heads}/{w.n_kv_heads} D={w.head_dim} "
+          f"Bs={w.block} prefix={prefix} density={density:.2f}", flush=True)
+    inp = wl.generate(w, prefix=prefix)
+    gpu, sels = run_gpu_sparse(inp, density)
+    ref = run_oracle_sparse(inp, sels)
+    for b, (g, r) in enumerate(zip(gpu, ref)):
+        H.compare_block(g, r, w.dtype, what=f"random-sparse {i} block {b}")
