@@ -399,9 +399,9 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     ext.load_state(p, bh);
     if constexpr (PREFETCH_EXT) ext.load_data(p, grow, hl);   // in flight with Q and the tiles
   }
-  // The lone-wave merge launch (short blocks: one tile) loads Q straight into
-  // registers, in flight with everything else; it waits for all loads before
-  // its first tile anyway.
+  // The lone-wave merge launch (blocks of fewer than 512 packed rows) loads Q
+  // straight into registers, in flight with everything else: issued before
+  // the tiles, those loads have landed once the first tile has.
   constexpr bool kQReg = MODE == kModeMerge && ROWW == 1 && PREFETCH_EXT;
   bf16x8 qf[D / 16];
   FB_LDS char* q_lds = lds + P::q_offset(P::ring_stages(p.ring_keys), ROWW) + rw * 32 * D * 2;
