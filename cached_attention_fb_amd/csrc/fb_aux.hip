@@ -1,6 +1,7 @@
 // Split combine, gamma decision and reset kernels (gfx950), and the attention
 // dispatcher.
 #include <algorithm>
+#include <type_traits>
 
 #include "fb_device.h"
 
@@ -33,6 +34,20 @@ __device__ __forceinline__ f32x4 load_part(const float* base, int64_t off) {
   } else {
     return *reinterpret_cast<const f32x4*>(base + off);
   }
+}
+// The same column as loaded, widened later by widen_part: a load that is to
+// stay in flight must not be converted at once (the conversion waits for it).
+template <bool PB>
+using PartRaw = std::conditional_t<PB, bf16x4, f32x4>;
+template <bool PB>
+__device__ __forceinline__ PartRaw<PB> load_part_raw(const float* base, int64_t off) {
+  if constexpr (PB) return *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(base) + off);
+  else return *reinterpret_cast<const f32x4*>(base + off);
+}
+template <bool PB>
+__device__ __forceinline__ f32x4 widen_part(const PartRaw<PB>& t) {
+  if constexpr (PB) return f32x4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
+  else return t;
 }
 
 template <int D, int BATCH, bool PB>
@@ -76,6 +91,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
         wsum = 1.0f;
         acc = *reinterpret_cast<const f32x4*>(p.slot_o + grow * D + 4 * c4);
       }
+    }
+    // A fused step's block-internal part, loaded before the rounds so that
+    // it arrives with them instead of one memory round trip after the fold.
+    float l_in = -INFINITY;
+    PartRaw<PB> a_in_raw{};
+    if (out_mode) {
+      l_in = lp[p.int_split * p.part_l_stride];
+      a_in_raw = load_part_raw<PB>(p.part_o, ao + p.int_split * p.part_o_stride);
     }
     // BATCH splits per round, all their loads in flight; past the last split
     // a round re-reads it and gives it no weight (L = -inf)
@@ -129,8 +152,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
       if (c4 == 0) *ld = lse;
     }
     if (out_mode) {   // the block-internal part (page §2 merge), then the step's output
-      const float l_in = lp[p.int_split * p.part_l_stride];
-      const f32x4 a_in = load_part<PB>(p.part_o, ao + p.int_split * p.part_o_stride);
+      const f32x4 a_in = widen_part<PB>(a_in_raw);
       const float nm = fmaxf(mx, l_in);
       if (nm > -INFINITY) {
         const float sc = fast_exp2((mx - nm) * kLog2e);
