@@ -101,35 +101,55 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
       a_in_raw = load_part_raw<PB>(p.part_o, ao + p.int_split * p.part_o_stride);
     }
     // BATCH splits per round, all their loads in flight; past the last split
-    // a round re-reads it and gives it no weight (L = -inf)
+    // a round re-reads it and gives it no weight (L = -inf).  The round's L
+    // values are spread over the row's lanes (lane c4 holds split s + c4, and
+    // s + c4 + kLpr, ...): one load per kLpr splits instead of one per split
+    // (a wave keeps at most 63 loads in flight), one exponential per split;
+    // the row max and weight sum are taken across the row's lanes and each
+    // weight is read from the lane that holds it.  Every lane still adds the
+    // splits' A in split order.
+    constexpr int kLl = (BATCH + kLpr - 1) / kLpr;   // L values per lane and round
     for (int s = 0; s < splits; s += BATCH) {
-      float l[BATCH];
-      f32x4 a[BATCH];
+      float lv[kLl];
+      PartRaw<PB> a[BATCH];   // widened where used: a conversion here would wait for its load
+#pragma unroll
+      for (int k = 0; k < kLl; ++k) {
+        const int u = c4 + kLpr * k;
+        const int si = min(s + u, splits - 1);
+        lv[k] = lp[si * p.part_l_stride];
+        if (u >= BATCH || s + u >= splits) lv[k] = -INFINITY;
+      }
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int si = min(s + u, splits - 1);
-        l[u] = lp[si * p.part_l_stride];
-        a[u] = load_part<PB>(p.part_o, ao + si * p.part_o_stride);
-        if (s + u >= splits) l[u] = -INFINITY;
+        a[u] = load_part_raw<PB>(p.part_o, ao + si * p.part_o_stride);
       }
       // keep every load of the round ahead of the arithmetic: left to itself
       // the scheduler trades the in-flight loads for registers and waits on
       // a few at a time
       __builtin_amdgcn_sched_barrier(0);
-      float cm = l[0];
+      float cm = lv[0];
 #pragma unroll
-      for (int u = 1; u < BATCH; ++u) cm = fmaxf(cm, l[u]);
+      for (int k = 1; k < kLl; ++k) cm = fmaxf(cm, lv[k]);
+#pragma unroll
+      for (int off = kLpr / 2; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kLpr));
       const float nm = fmaxf(mx, cm);
       if (nm > -INFINITY) {
         const float sc = fast_exp2((mx - nm) * kLog2e);
         acc *= sc;
         wsum *= sc;
+        float wv[kLl];
+        float ws = 0.0f;
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const float w = fast_exp2((l[u] - nm) * kLog2e);
-          wsum += w;
-          acc += w * a[u];
+        for (int k = 0; k < kLl; ++k) {
+          wv[k] = fast_exp2((lv[k] - nm) * kLog2e);
+          ws += wv[k];
         }
+#pragma unroll
+        for (int off = kLpr / 2; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, kLpr);
+        wsum += ws;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) acc += __shfl(wv[u / kLpr], u % kLpr, kLpr) * widen_part<PB>(a[u]);
         mx = nm;
       }
     }
