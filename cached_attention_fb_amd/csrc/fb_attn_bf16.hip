@@ -27,110 +27,67 @@ namespace fbk {
 
 namespace {
 
+// The K/V/Q DMA loads are issued from asm (see dma16), so the compiler does
+// not know about them: every wait for them is written here, in asm, and is a
+// compiler memory barrier, so that no LDS access moves across it.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that LDS accesses may not be moved across by the
+// compiler (the builtin alone does not order memory operations).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane DMA load HBM -> LDS (global_load_lds_dwordx4): lane i
+// writes dst + 16 i.  Issued from asm so that the compiler, unaware of it,
+// does not wait for every DMA load still in flight before each LDS read (it
+// would with the builtin, draining the tile ring).  AUX 2 = non-temporal.
+template <int AUX>
+__device__ __forceinline__ void dma16(FB_LDS char* dst, const void* src) {
+  static_assert(AUX == 0 || AUX == 2, "cache policy: default or non-temporal");
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  if constexpr (AUX == 2)
+    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(m0) : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// Plain LDS reads at a byte address; the compiler waits for them where their
+// values are first used.
+__device__ __forceinline__ u32x4 lds_b128(uint32_t a) { return *(const FB_LDS u32x4*)(size_t)a; }
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t a) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FB_LDS s16x4*)(size_t)a));
 }
 
 // Transposed LDS reads (ds_read_b64_tr_b16) of the V^T operands of one 32-key
-// half C (k-steps 2C and 2C+1, every head-dim tile, both 4-key sub-halves),
-// waited for inside the same asm block so the results have landed when it
-// ends.  Written in asm because with the builtin the compiler waits for every
-// DMA load still in flight before each read, which would drain the tile
-// pipeline.  base[dt] = the lane's offset for head-dim tile dt; k-step ks,
-// sub-half hf sits (16ks + 8hf) rows further.  r[(kl*kDt + dt)*2 + hf].
+// half C (k-steps 2C and 2C+1, every head-dim tile, both 4-key sub-halves).
+// base[dt] = the lane's offset for head-dim tile dt; k-step kl, sub-half hf
+// sits (32C + 16kl + 8hf) rows further.  r[(kl*kDt + dt)*2 + hf].
 template <int D, int C>
 __device__ __forceinline__ void tr_read_half(u32x2 (&r)[D / 8], const uint32_t (&base)[D / 32]) {
-  constexpr int o00 = (32 * C + 0) * D * 2, o01 = (32 * C + 8) * D * 2;
-  constexpr int o10 = (32 * C + 16) * D * 2, o11 = (32 * C + 24) * D * 2;
-  if constexpr (D == 128) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %2, %17 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %3, %17 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %4, %18 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %5, %18 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %6, %19 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %9, %16 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %10, %17 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %11, %17 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %12, %18 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %13, %18 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(o00), "i"(o01), "i"(o10), "i"(o11)
-        : "memory");
-  } else if constexpr (D == 64) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%11\n\t"
-        "ds_read_b64_tr_b16 %2, %9 offset:%10\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %6, %9 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(base[0]), "v"(base[1]), "i"(o00), "i"(o01), "i"(o10), "i"(o11)
-        : "memory");
+  constexpr int kDt = D / 32;
+#pragma unroll
+  for (int kl = 0; kl < 2; ++kl) {
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) r[(kl * kDt + dt) * 2 + hf] = lds_tr16(base[dt] + (32 * C + 16 * kl + 8 * hf) * D * 2);
+    }
   }
 }
 
-// Both 32-key halves' V^T operands in one asm block and one LDS wait (the
-// 8-row-wave shape, where each wave takes whole tiles): r0 = half 0, r1 =
-// half 1, each in the layout of tr_read_half.  One exposed LDS latency per
-// tile instead of two.
+// Both 32-key halves' V^T operands (the whole-tile shapes): r0 = half 0,
+// r1 = half 1, each in the layout of tr_read_half.
 template <int D>
 __device__ __forceinline__ void tr_read_both(u32x2 (&r0)[D / 8], u32x2 (&r1)[D / 8], const uint32_t (&base)[D / 32]) {
-  if constexpr (D == 128) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %32 offset:0\n\t"
-        "ds_read_b64_tr_b16 %1, %32 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %2, %33 offset:0\n\t"
-        "ds_read_b64_tr_b16 %3, %33 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %4, %34 offset:0\n\t"
-        "ds_read_b64_tr_b16 %5, %34 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %6, %35 offset:0\n\t"
-        "ds_read_b64_tr_b16 %7, %35 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %8, %32 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %9, %32 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %10, %33 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %11, %33 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %12, %34 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %13, %34 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %14, %35 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %15, %35 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %16, %32 offset:8192\n\t"
-        "ds_read_b64_tr_b16 %17, %32 offset:10240\n\t"
-        "ds_read_b64_tr_b16 %18, %33 offset:8192\n\t"
-        "ds_read_b64_tr_b16 %19, %33 offset:10240\n\t"
-        "ds_read_b64_tr_b16 %20, %34 offset:8192\n\t"
-        "ds_read_b64_tr_b16 %21, %34 offset:10240\n\t"
-        "ds_read_b64_tr_b16 %22, %35 offset:8192\n\t"
-        "ds_read_b64_tr_b16 %23, %35 offset:10240\n\t"
-        "ds_read_b64_tr_b16 %24, %32 offset:12288\n\t"
-        "ds_read_b64_tr_b16 %25, %32 offset:14336\n\t"
-        "ds_read_b64_tr_b16 %26, %33 offset:12288\n\t"
-        "ds_read_b64_tr_b16 %27, %33 offset:14336\n\t"
-        "ds_read_b64_tr_b16 %28, %34 offset:12288\n\t"
-        "ds_read_b64_tr_b16 %29, %34 offset:14336\n\t"
-        "ds_read_b64_tr_b16 %30, %35 offset:12288\n\t"
-        "ds_read_b64_tr_b16 %31, %35 offset:14336\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0[0]), "=&v"(r0[1]), "=&v"(r0[2]), "=&v"(r0[3]), "=&v"(r0[4]), "=&v"(r0[5]), "=&v"(r0[6]), "=&v"(r0[7]), "=&v"(r0[8]), "=&v"(r0[9]), "=&v"(r0[10]), "=&v"(r0[11]), "=&v"(r0[12]), "=&v"(r0[13]), "=&v"(r0[14]), "=&v"(r0[15]), "=&v"(r1[0]), "=&v"(r1[1]), "=&v"(r1[2]), "=&v"(r1[3]), "=&v"(r1[4]), "=&v"(r1[5]), "=&v"(r1[6]), "=&v"(r1[7]), "=&v"(r1[8]), "=&v"(r1[9]), "=&v"(r1[10]), "=&v"(r1[11]), "=&v"(r1[12]), "=&v"(r1[13]), "=&v"(r1[14]), "=&v"(r1[15])
-        : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3])
-        : "memory");
-  } else {
-    tr_read_half<D, 0>(r0, base);
-    tr_read_half<D, 1>(r1, base);
-  }
+  tr_read_half<D, 0>(r0, base);
+  tr_read_half<D, 1>(r1, base);
 }
 
 // Wait until at most `after` tiles' DMA loads (kLpt per tile and wave) are
@@ -151,72 +108,22 @@ __device__ __forceinline__ void wait_tile(int after) {
 }
 
 // K^T operand fragments of one 32-key half: 16-byte chunk 2t + hl of the
-// lane's key row, t = 0..D/16-1, read with ds_read_b128 and waited for inside
-// the same asm block (one LDS wait per half instead of one per MFMA; asm for
-// the same reason as the transposed reads).  a[t] = row/chunk offset of the
-// lane in the stage, OFF = the half's offset (32 rows per half).
+// lane's key row, t = 0..D/16-1 (ds_read_b128).  a[t] = row/chunk offset of
+// the lane in the stage, OFF = the half's offset (32 rows per half).
 template <int D, int OFF>
 __device__ __forceinline__ void k_read_half(u32x4 (&r)[D / 16], const uint32_t (&a)[D / 16]) {
-  if constexpr (D == 128) {
-    asm volatile(
-        "ds_read_b128 %0, %8 offset:%16\n\t"
-        "ds_read_b128 %1, %9 offset:%16\n\t"
-        "ds_read_b128 %2, %10 offset:%16\n\t"
-        "ds_read_b128 %3, %11 offset:%16\n\t"
-        "ds_read_b128 %4, %12 offset:%16\n\t"
-        "ds_read_b128 %5, %13 offset:%16\n\t"
-        "ds_read_b128 %6, %14 offset:%16\n\t"
-        "ds_read_b128 %7, %15 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
-        : "memory");
-  } else if constexpr (D == 64) {
-    asm volatile(
-        "ds_read_b128 %0, %4 offset:%8\n\t"
-        "ds_read_b128 %1, %5 offset:%8\n\t"
-        "ds_read_b128 %2, %6 offset:%8\n\t"
-        "ds_read_b128 %3, %7 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
-        : "memory");
-  }
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) r[t] = lds_b128(a[t] + OFF);
 }
 
-// Both halves' K^T operand fragments in one asm block and one LDS wait
-// (r0 = keys 0-31 of the tile, r1 = keys 32-63), as k_read_half.
+// Both halves' K^T operand fragments (r0 = keys 0-31 of the tile, r1 = keys
+// 32-63), as k_read_half.
 template <int D>
 __device__ __forceinline__ void k_read_both(u32x4 (&r0)[D / 16], u32x4 (&r1)[D / 16], const uint32_t (&a)[D / 16]) {
-  if constexpr (D == 128) {
-    constexpr int H = 32 * D * 2;
-    asm volatile(
-        "ds_read_b128 %0, %16\n\t"
-        "ds_read_b128 %1, %17\n\t"
-        "ds_read_b128 %2, %18\n\t"
-        "ds_read_b128 %3, %19\n\t"
-        "ds_read_b128 %4, %20\n\t"
-        "ds_read_b128 %5, %21\n\t"
-        "ds_read_b128 %6, %22\n\t"
-        "ds_read_b128 %7, %23\n\t"
-        "ds_read_b128 %8, %16 offset:%24\n\t"
-        "ds_read_b128 %9, %17 offset:%24\n\t"
-        "ds_read_b128 %10, %18 offset:%24\n\t"
-        "ds_read_b128 %11, %19 offset:%24\n\t"
-        "ds_read_b128 %12, %20 offset:%24\n\t"
-        "ds_read_b128 %13, %21 offset:%24\n\t"
-        "ds_read_b128 %14, %22 offset:%24\n\t"
-        "ds_read_b128 %15, %23 offset:%24\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0[0]), "=&v"(r0[1]), "=&v"(r0[2]), "=&v"(r0[3]), "=&v"(r0[4]), "=&v"(r0[5]), "=&v"(r0[6]), "=&v"(r0[7]),
-          "=&v"(r1[0]), "=&v"(r1[1]), "=&v"(r1[2]), "=&v"(r1[3]), "=&v"(r1[4]), "=&v"(r1[5]), "=&v"(r1[6]), "=&v"(r1[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(H)
-        : "memory");
-  } else {
-    k_read_half<D, 0>(r0, a);
-    k_read_half<D, 32 * D * 2>(r1, a);
-  }
+  k_read_half<D, 0>(r0, a);
+  k_read_half<D, 32 * D * 2>(r1, a);
 }
+
 
 // P = exp2(c*s - mref) of one S^T half, its contribution to the lane's row
 // sum, and the bf16 B operands of its two k-steps (registers j = 8kl .. 8kl+7).
@@ -285,9 +192,9 @@ __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, c
     const int pos = ii * 64 + lane;                 // 16-byte slot inside the tile
     const int key = pos / P::kCpr, pc = pos % P::kCpr;
     const int swz = tensor == 0 ? (key & (P::kCpr - 1)) : ((4 * key) & (P::kCpr - 4));
-    const int gk = min(tile0 + key, key_end - 1);   // rows past the end: any valid row (masked later)
+    const int gk = max(0, min(tile0 + key, key_end - 1));   // rows past the end: any valid row (masked later)
     const bf16* src = (tensor == 0 ? kb : vb) + (int64_t)gk * D + (pc ^ swz) * 8;
-    __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(stage + tensor * P::kTensorBytes + ii * 1024), 16, 0, AUX);
+    dma16<AUX>(stage + tensor * P::kTensorBytes + ii * 1024, src);
   }
 }
 
@@ -301,7 +208,7 @@ __device__ __forceinline__ void issue_q(FB_LDS char* dst, const bf16* q_rows, in
   for (int j = 0; j < 32 * kCpr / 64; ++j) {
     const int pos = j * 64 + lane, r = pos / kCpr, pc = pos % kCpr;
     const bf16* src = q_rows + (int64_t)min(r, rows_left - 1) * D + (pc ^ (r & (kCpr - 1))) * 8;
-    __builtin_amdgcn_global_load_lds(src, (FB_LDS void*)(dst + j * 1024), 16, 0, 0);
+    dma16<0>(dst + j * 1024, src);
   }
 }
 
@@ -426,7 +333,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     issued = 0;
     wait_vmcnt<0>();
   }
-  __builtin_amdgcn_s_barrier();   // every wave's share of tile 0 (and Q) landed
+  lds_barrier();   // every wave's share of tile 0 (and Q) landed
   // Q^T as the B operand: lane (row, hl) holds Q[row][16t + 8hl .. +7].
   if constexpr (!kQReg) {
     uint32_t qa[D / 16];
@@ -440,7 +347,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   }
   // When Q sits in ring stages 2-3, every wave must have read it before the
   // first refill writes there (past the ring it needs no barrier).
-  if (!P::q_past(ROWW) && P::ring_stages(p.ring_keys) == P::kStages) __builtin_amdgcn_s_barrier();
+  if (!P::q_past(ROWW) && P::ring_stages(p.ring_keys) == P::kStages) lds_barrier();
 
   f32x16 o[kDt];
 #pragma unroll
@@ -475,7 +382,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   for (int t_i = 0; t_i < ntiles; ++t_i) {
     if (t_i > 0) {
       wait_tile<P::kLpt, P::kStages>(issued - t_i - 1);   // tiles issued after this one may stay in flight
-      __builtin_amdgcn_s_barrier();   // every wave's share landed; all waves finished tile t_i-1
+      lds_barrier();   // every wave's share landed; all waves finished tile t_i-1
     }
     if (wave_live) {
       const int tile0 = tm.key0(t_i);
@@ -488,17 +395,36 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
       for (int t = 0; t < D / 16; ++t) ka[t] = ks_off + k_off[t];
       f32x16 s[NH];
       const int nh_live = (kShortSkip && tile0 + 32 >= lim) ? 1 : NH;
+      uint32_t vbase[kDt];
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) vbase[dt] = vs_off + tr_off[dt];
+      u32x2 vr[D / 8];
+      u32x2 vr1[D / 8];
       if constexpr (NH == 2 && ROWW > 1) {
-        // both halves' K fragments in one batched read (one LDS wait per
-        // tile), then the two independent S chains interleaved
+        // Whole tiles: the K fragments of both halves (in the order the two
+        // interleaved S chains use them) and then both halves' V^T operands
+        // are read while the S MFMAs run; the scheduler is told to issue a
+        // few LDS reads after every MFMA, so the reads hide under the MFMAs
+        // and the compiler waits for each fragment only where it is used.
         u32x4 kf0[D / 16], kf1[D / 16];
-        k_read_both<D>(kf0, kf1, ka);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          kf0[t] = lds_b128(ka[t]);
+          kf1[t] = lds_b128(ka[t] + 32 * D * 2);
+        }
+        tr_read_both<D>(vr, vr1, vbase);
         s[0] = f32x16{};
         s[1] = f32x16{};
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
           s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf0[t]), qf[t], s[0], 0, 0, 0);
           s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf1[t]), qf[t], s[1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // the first LDS reads
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // then up to three LDS reads
         }
       } else {
 #pragma unroll
@@ -558,15 +484,11 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
         }
       }
       const float mref = m > -INFINITY ? m : 0.0f;   // a row with no key yet (second half of a short block)
-      uint32_t vbase[kDt];
-#pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) vbase[dt] = vs_off + tr_off[dt];
-      u32x2 vr[D / 8];
-      u32x2 vr1[D / 8];
       bf16x8 pb0[2];
-      if constexpr (NH == 2 && ROWW > 1) tr_read_both<D>(vr, vr1, vbase);
-      else if (kh * NH == 0) tr_read_half<D, 0>(vr, vbase);
-      else tr_read_half<D, 1>(vr, vbase);
+      if constexpr (!(NH == 2 && ROWW > 1)) {   // (whole tiles: read with K above)
+        if (kh * NH == 0) tr_read_half<D, 0>(vr, vbase);
+        else tr_read_half<D, 1>(vr, vbase);
+      }
       exp_half(s[0], mref, p.scale_log2, lsum, pb0);
       if (kShortSkip && nh_live == 1) {
         pv_half<kDt>(o, vr, pb0);   // the second half holds no key (short block)
@@ -614,7 +536,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     // (the last tile waited for vmcnt 0), so the ring can be reused.
     constexpr int kChunks = 4 * kDt + 1;
     FB_LDS f32x4* xch = (FB_LDS f32x4*)lds + rw * kChunks * 64 + lane;
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     if (kh == 1 && wave_live) {
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
@@ -624,7 +546,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
       }
       xch[(4 * kDt) * 64] = f32x4{m, lsum, 0.0f, 0.0f};
     }
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     if (kh == 1) return;
     if (wave_live) {
       const f32x4 ml = xch[(4 * kDt) * 64];
@@ -653,7 +575,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     // scattered 32-byte pieces.  Waves use disjoint regions, so after the
     // ring is released (barrier below, or the exchange above) no further
     // synchronisation is needed.
-    if constexpr (KSPLIT == 1) __builtin_amdgcn_s_barrier();   // every wave finished reading the ring
+    if constexpr (KSPLIT == 1) lds_barrier();   // every wave finished reading the ring
     if (!wave_live) return;
     const float ltot = pair_sum(lsum);
     constexpr int kRegionFloats = KSPLIT == 2 ? (4 * kDt + 1) * 64 * 4 : 32 * D;
