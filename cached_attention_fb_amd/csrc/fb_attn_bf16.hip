@@ -333,6 +333,13 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     issued = 0;
     wait_vmcnt<0>();
   }
+  if constexpr (kQReg) {
+    // Q's register loads were issued before the tiles, so they have landed;
+    // the compiler, which does not count the DMA loads, would otherwise wait
+    // for them inside the loop with counts that drain the ring every tile.
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) asm volatile("" : "+v"(qf[t]));
+  }
   lds_barrier();   // every wave's share of tile 0 (and Q) landed
   // Q^T as the B operand: lane (row, hl) holds Q[row][16t + 8hl .. +7].
   if constexpr (!kQReg) {
@@ -426,18 +433,56 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // then up to three LDS reads
         }
-      } else {
+      } else if constexpr (NH == 1) {
+        // Key halves: this wave's half of K and of V^T read under its S
+        // MFMAs, as above (the half's offset added, not branched on, so that
+        // the reads and the MFMAs share one scheduling region).
+        const uint32_t hoff = kh * (32 * D * 2);
+        uint32_t kh_a[D / 16], kh_v[kDt];
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        s[h] = f32x16{};
-        if (h >= nh_live) continue;
+        for (int t = 0; t < D / 16; ++t) kh_a[t] = ka[t] + hoff;
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) kh_v[dt] = vbase[dt] + hoff;
         u32x4 kf[D / 16];
-        if (kh * NH + h == 0) k_read_half<D, 0>(kf, ka);
-        else k_read_half<D, 32 * D * 2>(kf, ka);
+        k_read_half<D, 0>(kf, kh_a);
+        tr_read_half<D, 0>(vr, kh_v);
+        s[0] = f32x16{};
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[h], 0, 0, 0);
-      }
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[0], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // the first LDS reads
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // then up to three LDS reads
+        }
+      } else {
+        // The lone wave of short blocks: half 0's K and V^T read under its S
+        // MFMAs (as above; half 1's V^T is read after its exponentials), and
+        // a half 1 with no key is skipped.
+        u32x4 kf[D / 16];
+        k_read_half<D, 0>(kf, ka);
+        tr_read_half<D, 0>(vr, vbase);
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t]), qf[t], s[0], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // the first LDS reads
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // then up to three LDS reads
+        }
+        if (nh_live > 1) {
+          u32x4 kf1[D / 16];
+          k_read_half<D, 32 * D * 2>(kf1, ka);
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t)
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf1[t]), qf[t], s[1], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);   // all its K reads (one wait),
+          __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);   // then its MFMAs
+        }
       }
       // Ragged last tile: keys at or past the limit do not count.  In the
       // single-wave kernels (short blocks: often one tile, often half full) a
@@ -485,10 +530,6 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
       }
       const float mref = m > -INFINITY ? m : 0.0f;   // a row with no key yet (second half of a short block)
       bf16x8 pb0[2];
-      if constexpr (!(NH == 2 && ROWW > 1)) {   // (whole tiles: read with K above)
-        if (kh * NH == 0) tr_read_half<D, 0>(vr, vbase);
-        else tr_read_half<D, 1>(vr, vbase);
-      }
       exp_half(s[0], mref, p.scale_log2, lsum, pb0);
       if (kShortSkip && nh_live == 1) {
         pv_half<kDt>(o, vr, pb0);   // the second half holds no key (short block)
