@@ -48,14 +48,37 @@ __device__ __forceinline__ void lds_barrier() {
 // writes dst + 16 i.  Issued from asm so that the compiler, unaware of it,
 // does not wait for every DMA load still in flight before each LDS read (it
 // would with the builtin, draining the tile ring).  AUX 2 = non-temporal.
+// The compiler does not look inside asm for hazards, so the asm supplies the
+// wait states itself: the LDS address comes from M0, which the compiler sets
+// just before with a scalar instruction, and an LDS DMA needs one wait state
+// after a scalar write of M0.
 template <int AUX>
 __device__ __forceinline__ void dma16(FB_LDS char* dst, const void* src) {
   static_assert(AUX == 0 || AUX == 2, "cache policy: default or non-temporal");
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
   if constexpr (AUX == 2)
-    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(m0) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(m0) : "memory");
   else
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// The same load with a wave-uniform base address (SGPRs) and a per-lane 32-bit
+// byte offset (the saddr form), so that a lane adds no 64-bit address.  The
+// base must be the same in every lane (it is read from the first).  The base
+// SGPRs may be written by a vector instruction (v_readfirstlane) right before,
+// and a memory instruction may read such an SGPR only 5 wait states later:
+// the asm waits them out (they also cover the M0 write).
+template <int AUX>
+__device__ __forceinline__ void dma16s(FB_LDS char* dst, const void* base_any, uint32_t voff) {
+  static_assert(AUX == 0 || AUX == 2, "cache policy: default or non-temporal");
+  const uint64_t a = (uint64_t)(uintptr_t)base_any;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const void* base = (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  if constexpr (AUX == 2)
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+  else
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
 }
 
 // Plain LDS reads at a byte address; the compiler waits for them where their
@@ -180,10 +203,45 @@ struct Pipe {
 
 // AUX: cache policy of the DMA loads (2: non-temporal, for K/V that no other
 // workgroup of the launch reads again).
+//
+// A whole tile (every key below key_end) takes the short form: instruction ii
+// covers keys kKpi*ii + key_l (key_l = lane / (D/8)), so its base is uniform
+// and the lane's offset depends on ii only through the K swizzle, whose
+// ii-part is a multiple of kKpi while key_l < kKpi:
+//   K chunk pc ^ ((kKpi*ii + key_l) % (D/8)) = (pc ^ key_l) ^ ((kKpi*ii) % (D/8)),
+//   V chunk pc ^ ((4*key) % (D/8) & ~3) = pc ^ (4*key_l % (D/8)) (4*kKpi*ii is
+//   a multiple of D/8).
+// A ragged tile clamps every key to the last valid one.
 template <int D, int WAVES, int AUX>
 __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, const bf16* vb, int tile0,
                                            int key_end, int wave, int lane) {
   using P = Pipe<D, WAVES>;
+  constexpr int kKpi = 64 / P::kCpr;   // keys per DMA instruction
+  static_assert(P::kCpr % kKpi == 0 && P::kCpr <= 16, "the swizzles split into a uniform and a per-lane part");
+  if (tile0 + kKeyTile <= key_end) {
+    const int key_l = lane / P::kCpr, pc = lane % P::kCpr;
+    const uint32_t row_b = key_l * D * 2;
+    const uint32_t k_c = (pc ^ key_l) * 16;
+    const uint32_t v_off = row_b + (pc ^ ((4 * key_l) & (P::kCpr - 4))) * 16;
+    // A wave's instructions are consecutive: with several waves they lie in
+    // one tensor (ii = ii0 + j), a lone wave issues all of them (ii = j % kIPT).
+    constexpr int kIPT = P::kInstrPerTensor;
+    static_assert(WAVES == 1 || kIPT % P::kLpt == 0, "a wave's loads stay in one tensor");
+    const int idx0 = wave * P::kLpt;
+    const int tensor_w = idx0 / kIPT, ii0 = idx0 % kIPT;
+    const bf16* base0 = (tensor_w == 0 ? kb : vb) + (int64_t)(tile0 + kKpi * ii0) * D;
+    FB_LDS char* dst0 = stage + tensor_w * P::kTensorBytes + ii0 * 1024;
+#pragma unroll
+    for (int j = 0; j < P::kLpt; ++j) {
+      const int tensor = WAVES == 1 ? j / kIPT : tensor_w;
+      const int ii = WAVES == 1 ? j % kIPT : ii0 + j;
+      const bf16* base = WAVES == 1 ? (tensor == 0 ? kb : vb) + (int64_t)(tile0 + kKpi * ii) * D : base0 + j * kKpi * D;
+      FB_LDS char* dst = WAVES == 1 ? stage + tensor * P::kTensorBytes + ii * 1024 : dst0 + j * 1024;
+      const uint32_t voff = tensor == 0 ? row_b + (k_c ^ (((kKpi * ii) & (P::kCpr - 1)) * 16)) : v_off;
+      dma16s<AUX>(dst, base, voff);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < P::kLpt; ++j) {
     const int idx = wave * P::kLpt + j;
@@ -201,9 +259,18 @@ __device__ __forceinline__ void issue_tile(FB_LDS char* stage, const bf16* kb, c
 // The wave's 32 query rows into LDS ([32][D], the K tile layout: 16-byte
 // chunk c of row r at c ^ (r % (D/8))), so that they are read like a K half.
 // Rows at or past rows_left repeat the last valid row.
+// With all 32 rows valid, the short form of issue_tile's K (rows for keys).
 template <int D>
 __device__ __forceinline__ void issue_q(FB_LDS char* dst, const bf16* q_rows, int rows_left, int lane) {
-  constexpr int kCpr = D / 8;
+  constexpr int kCpr = D / 8, kKpi = 64 / kCpr;
+  if (rows_left >= 32) {
+    const int key_l = lane / kCpr, pc = lane % kCpr;
+    const uint32_t row_b = key_l * D * 2, k_c = (pc ^ key_l) * 16;
+#pragma unroll
+    for (int j = 0; j < 32 * kCpr / 64; ++j)
+      dma16s<0>(dst + j * 1024, q_rows + (int64_t)(kKpi * j) * D, row_b + (k_c ^ (((kKpi * j) & (kCpr - 1)) * 16)));
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 32 * kCpr / 64; ++j) {
     const int pos = j * 64 + lane, r = pos / kCpr, pc = pos % kCpr;
@@ -266,7 +333,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   FB_LDS char* lds = (FB_LDS char*)smem_raw;
 
   prefetch_params(p);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rw = wave % ROWW, kh = wave / ROWW;
   const int rl = lane & 31, hl = lane >> 5;
   // ONE: a 3-D grid (row tile, kv head, sequence), one key range per group
