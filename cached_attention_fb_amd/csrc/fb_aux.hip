@@ -50,6 +50,55 @@ __device__ __forceinline__ f32x4 widen_part(const PartRaw<PB>& t) {
   else return t;
 }
 
+// Reductions and broadcasts inside a group of W = 16 or 32 consecutive lanes
+// (one combine row), on the vector ALUs: DPP rotations within a 16-lane row
+// (each step adds the same pair of values in both lanes, so every lane of
+// the group ends with the bitwise-same result) and, for 32 lanes, a swap of
+// the two rows.  A shuffle through the LDS unit would wait out its latency
+// at every step.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(W == 16 || W == 32, "a combine row is 16 or 32 lanes");
+  x = fmaxf(x, row_ror<8>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  x = fmaxf(x, row_ror<1>(x));
+  if constexpr (W == 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return x;
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(W == 16 || W == 32, "a combine row is 16 or 32 lanes");
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
+  if constexpr (W == 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+// Value of lane j (wave-uniform) of this lane's W-lane group: read from every
+// group of the wave with v_readlane and the lane's own group selected.
+template <int W>
+__device__ __forceinline__ float group_bcast(float x, int j, int group) {
+  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+#pragma unroll
+  for (int g = 1; g < 64 / W; ++g) {
+    const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), g * W + j));
+    v = group == g ? o : v;
+  }
+  return v;
+}
+
 template <int D, int BATCH, bool PB>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p) {
   constexpr int kLpr = D / 4;
@@ -106,7 +155,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     // s + c4 + kLpr, ...): one load per kLpr splits instead of one per split
     // (a wave keeps at most 63 loads in flight), one exponential per split;
     // the row max and weight sum are taken across the row's lanes and each
-    // weight is read from the lane that holds it.  Every lane still adds the
+    // weight is read from the lane that holds it (vector-ALU cross-lane
+    // operations, see group_max).  Every lane still adds the
     // splits' A in split order.
     constexpr int kLl = (BATCH + kLpr - 1) / kLpr;   // L values per lane and round
     for (int s = 0; s < splits; s += BATCH) {
@@ -131,8 +181,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
       float cm = lv[0];
 #pragma unroll
       for (int k = 1; k < kLl; ++k) cm = fmaxf(cm, lv[k]);
-#pragma unroll
-      for (int off = kLpr / 2; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kLpr));
+      cm = group_max<kLpr>(cm);
       const float nm = fmaxf(mx, cm);
       if (nm > -INFINITY) {
         const float sc = fast_exp2((mx - nm) * kLog2e);
@@ -145,11 +194,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
           wv[k] = fast_exp2((lv[k] - nm) * kLog2e);
           ws += wv[k];
         }
+        wsum += group_sum<kLpr>(ws);
+        const int grp_w = (tid & 63) / kLpr;   // this lane's row within the wave
 #pragma unroll
-        for (int off = kLpr / 2; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, kLpr);
-        wsum += ws;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) acc += __shfl(wv[u / kLpr], u % kLpr, kLpr) * widen_part<PB>(a[u]);
+        for (int u = 0; u < BATCH; ++u) acc += group_bcast<kLpr>(wv[u / kLpr], u % kLpr, grp_w) * widen_part<PB>(a[u]);
         mx = nm;
       }
     }
