@@ -9,12 +9,6 @@ namespace fbk {
 
 namespace {
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
 // Split combine (page §2's log-space rule over the prefix chunks):
 // A = sum_s e^{L_s - M} A_s / sum_s e^{L_s - M}, L = M + log sum, M = max_s L_s.
 // One wave per workgroup, D/4 lanes (one float4 column each) per row.  The
@@ -86,6 +80,14 @@ __device__ __forceinline__ float group_sum(float x) {
   }
   return x;
 }
+// Sum over the whole wave (every lane gets the same value): the 32-lane
+// groups, then the two halves swapped and added.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<32>(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Value of lane j (wave-uniform) of this lane's W-lane group: read from every
 // group of the wave with v_readlane and the lane's own group selected.
 template <int W>
