@@ -14,14 +14,24 @@ SOURCES = ["fb_attn_bf16.hip", "fb_attn_f32.hip", "fb_aux.hip", "fb_runtime.cpp"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+COMPILE_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17",
+    # keep fp32 arithmetic off the packed-fp32 VALU forms
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the softmax works on them without AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
 def hipcc_command(out=LIB, extra=()):
-    return [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-            # keep fp32 arithmetic off the packed-fp32 VALU forms
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # MFMA results in VGPRs: the softmax works on them without AGPR copies
-            "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    return [HIPCC, *COMPILE_FLAGS, "-fPIC", "-shared",
             *[os.path.join(CSRC, s) for s in SOURCES], *extra, "-o", out]
+
+
+def device_asm_command(source, out):
+    """The gfx950 assembly of one source file, built with the library's flags."""
+    return [HIPCC, *COMPILE_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, source), "-o", out]
 
 
 def build(verbose=False):

@@ -1,0 +1,67 @@
+"""Properties of the kernels' gfx950 assembly (built here from the sources,
+with the library's own flags), checked without a GPU.
+
+- Every K/V/Q DMA load (global_load_lds_dwordx4, issued from inline asm, where
+  the compiler's hazard checks do not reach) is directly preceded by the wait
+  states it needs: one after the scalar write of M0 that sets its LDS
+  address, five where its SGPR base may have been written by a vector
+  instruction just before.  A missing wait reads a stale register: the load
+  goes to a wrong address.
+- No packed-fp32 vector instruction (v_pk_add/mul/fma_f32) appears: the
+  build turns the feature off and no code writes them by hand.
+- The attention kernels use no scratch memory (nothing spills).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from cached_attention_fb_amd import build as B
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
+                                reason="hipcc is not installed")
+
+
+def _asm(source, tmp_path):
+    out = str(tmp_path / (source + ".s"))
+    r = subprocess.run(B.device_asm_command(source, out), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return [l.strip() for l in open(out).read().splitlines()]
+
+
+@pytest.fixture(scope="module")
+def attn_asm(tmp_path_factory):
+    return _asm("fb_attn_bf16.hip", tmp_path_factory.mktemp("asm"))
+
+
+def _instructions(lines):
+    return [l for l in lines if l and not l.startswith((";", ".", "#")) and not l.endswith(":")]
+
+
+def test_dma_loads_carry_their_wait_states(attn_asm):
+    ins = _instructions(attn_asm)
+    loads = [i for i, l in enumerate(ins) if l.startswith("global_load_lds_dwordx4")]
+    assert len(loads) > 100   # the attention kernels issue their tiles this way
+    for i in loads:
+        uniform_base = re.search(r",\s*s\[\d+:\d+\]", ins[i]) is not None
+        need = "s_nop 4" if uniform_base else "s_nop 0"
+        assert ins[i - 1] == need, f"{ins[i]!r} preceded by {ins[i - 1]!r}, needs {need}"
+
+
+def test_no_packed_fp32_instructions(attn_asm, tmp_path):
+    for name, lines in (("fb_attn_bf16.hip", attn_asm), ("fb_aux.hip", _asm("fb_aux.hip", tmp_path)),
+                        ("fb_attn_f32.hip", _asm("fb_attn_f32.hip", tmp_path))):
+        bad = [l for l in _instructions(lines) if re.match(r"v_pk_(add|mul|fma)_f32\b", l)]
+        assert not bad, f"{name}: {bad[:3]}"
+
+
+def test_attention_kernels_do_not_spill(attn_asm):
+    kernels = [l.split()[1] for l in attn_asm if l.startswith(".amdhsa_kernel ")]
+    assert kernels
+    text = "\n".join(attn_asm)
+    sizes = re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)
+    assert len(sizes) == len(kernels)
+    assert all(int(s) == 0 for s in sizes), list(zip(kernels, sizes))
+    assert not any(l.startswith("scratch_") for l in _instructions(attn_asm))
