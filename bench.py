@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -47,15 +48,23 @@ MALL_BYTES = 256 << 20
 EXTRA = ["long-32k-b4", "max-128k", "video-1560x15600", "tiny-fp32"]
 
 
+def _code_text(src: str) -> str:
+    """Source text without comments and with whitespace collapsed: what the
+    compiler sees (no string literal in the kernel sources holds // or /*)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources: stored traffic counters apply only to the
-    kernels they were taken on."""
+    """Hash of the kernel sources' code (comments and layout ignored): stored
+    traffic counters apply only to the kernels they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "cached_attention_fb_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update(name.encode() + _code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

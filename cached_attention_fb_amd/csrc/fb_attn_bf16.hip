@@ -364,8 +364,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   // and the first two tiles (more would only queue behind them in the memory
   // system while the first is awaited), all three through the LDS DMA path.
   // Q goes through LDS rather than straight into registers because the
-  // compiler cannot order register loads against the DMA loads and would
-  // drain the whole ring before every MFMA that reads Q (except in the
+  // compiler, which counts its register loads but not the DMA loads, would
+  // wait for Q with counts that drain the whole ring (except in the
   // lone-wave merge launch, see below).
   ExtPart<D> ext;
   const bool ext_lane = MODE == kModeMerge && row_ok && kh == 0;
@@ -462,8 +462,8 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
       const int tile0 = tm.key0(t_i);
       const uint32_t ks_off = lds_off + (t_i % P::kStages) * P::kStageBytes;
       const uint32_t vs_off = ks_off + P::kTensorBytes;
-      // S^T, one 32-key half at a time: the half's K fragments in one batched
-      // LDS read, then its MFMA chain over the head dimension.
+      // S^T = K Q^T per 32-key half: the half's K fragments, then its MFMA
+      // chain over the head dimension (LDS byte addresses of the fragments).
       uint32_t ka[D / 16];
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) ka[t] = ks_off + k_off[t];
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
       if (kShortSkip && nh_live == 1) {
         pv_half<kDt>(o, vr, pb0);   // the second half holds no key (short block)
       } else if constexpr (NH == 2 && ROWW > 1) {
-        // half 1's V^T was read with half 0's (one LDS wait); its
+        // half 1's V^T was read with half 0's, under the S MFMAs; its
         // exponentials are interleaved with half 0's PV MFMAs
         bf16x8 pb1[2];
         pv_half<kDt>(o, vr, pb0);
