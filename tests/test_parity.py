@@ -86,6 +86,11 @@ CASES = [
     Case("bf16", 64, 4, 4, 16, 700),         # D=64 in the one-wave shape
     Case("bf16", 64, 4, 1, 200, 900),        # D=64, 8-row-wave shape, 4 row tiles
     Case("bf16", 128, 16, 2, 40, 2000),      # GQA 8, 2 row tiles
+    # the two forms of the K/V/Q DMA addressing: whole tiles and a full
+    # 32-row Q block (uniform base + lane offsets) vs ragged ones (clamped)
+    Case("bf16", 128, 4, 1, 8, 4096, splits=4),   # 32 packed rows, every tile whole
+    Case("bf16", 128, 1, 1, 31, 4095, splits=3),  # 31 rows, ragged last tile
+    Case("bf16", 64, 4, 1, 8, 2048, splits=4),    # D=64, 32 rows, every tile whole
 ]
 
 
