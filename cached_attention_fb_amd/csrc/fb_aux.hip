@@ -107,8 +107,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
   constexpr int kRows = kCombineThreads / kLpr;
   prefetch_params(p);
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x / p.row_chunks, ch = blockIdx.x % p.row_chunks;
-  const int b = bh / p.hq;
+  // 3-D grid (row chunk, query head, sequence): no division
+  const int ch = blockIdx.x, b = blockIdx.z;
+  const int bh = b * p.hq + blockIdx.y;
   const bool out_mode = p.out != nullptr;
   const bool sel = head_selected(p.sel, b, bh);
   if (p.cum != nullptr && bh % p.hq == 0 && ch == 0 && tid == 0) {   // once per sequence
@@ -374,11 +375,12 @@ hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, h
 }
 
 template <int D, bool PB>
-hipError_t launch_combine_batch(int most, int blocks, const CombineParams& p, hipStream_t s);
+hipError_t launch_combine_batch(int most, dim3 grid, const CombineParams& p, hipStream_t s);
 
 hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s) {
-  const int blocks = p.batch * p.hq * p.row_chunks;
-  if (blocks == 0) return hipSuccess;
+  if (p.batch * p.hq * p.row_chunks == 0) return hipSuccess;
+  if (p.hq > 65535 || p.batch > 65535) return hipErrorInvalidValue;   // grid y / z limits
+  const dim3 blocks(p.row_chunks, p.hq, p.batch);   // launch order = (sequence, head, chunk)
   // one memory round trip per BATCH splits: the smallest batch that holds the
   // largest split count this launch can see (the device plan's too)
   int most = p.splits;
@@ -392,10 +394,10 @@ hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s) {
 }
 
 template <int D, bool PB>
-hipError_t launch_combine_batch(int most, int blocks, const CombineParams& p, hipStream_t s) {
-  if (most <= 8) hipLaunchKernelGGL((combine_kernel<D, 8, PB>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
-  else if (most <= 16) hipLaunchKernelGGL((combine_kernel<D, 16, PB>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
-  else hipLaunchKernelGGL((combine_kernel<D, 32, PB>), dim3(blocks), dim3(kCombineThreads), 0, s, p);
+hipError_t launch_combine_batch(int most, dim3 blocks, const CombineParams& p, hipStream_t s) {
+  if (most <= 8) hipLaunchKernelGGL((combine_kernel<D, 8, PB>), blocks, dim3(kCombineThreads), 0, s, p);
+  else if (most <= 16) hipLaunchKernelGGL((combine_kernel<D, 16, PB>), blocks, dim3(kCombineThreads), 0, s, p);
+  else hipLaunchKernelGGL((combine_kernel<D, 32, PB>), blocks, dim3(kCombineThreads), 0, s, p);
   return hipGetLastError();
 }
 
