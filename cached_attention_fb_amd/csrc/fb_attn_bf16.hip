@@ -726,7 +726,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
   lds = std::max(lds, kStageOut);
   hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX, ONE>), grid, dim3(64 * ROWW * KSPLIT),
-                     lds, s, p);
+                     lds, s, with_div_magic(p, blocks));
   return hipGetLastError();
 }
 

@@ -123,10 +123,11 @@ template <int D>
 hipError_t launch_d(int mode, const AttnParams& p, hipStream_t s) {
   const int blocks = p.grid > 0 ? p.grid : p.batch * p.hkv * p.splits * p.row_tiles;
   if (blocks == 0) return hipSuccess;
+  const AttnParams q = with_div_magic(p, blocks);
   if (mode == kModePartial)
-    hipLaunchKernelGGL((attn_f32_kernel<D, kModePartial>), dim3(blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_f32_kernel<D, kModePartial>), dim3(blocks), dim3(kThreads), 0, s, q);
   else
-    hipLaunchKernelGGL((attn_f32_kernel<D, kModeMerge>), dim3(blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_f32_kernel<D, kModeMerge>), dim3(blocks), dim3(kThreads), 0, s, q);
   return hipGetLastError();
 }
 

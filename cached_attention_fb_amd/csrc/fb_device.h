@@ -104,6 +104,12 @@ __device__ __forceinline__ uint64_t active_groups(const HeadSel& sel, int groups
   return __builtin_amdgcn_ballot_w64(act);
 }
 
+// n / d for a grid index, with m from div_magic (0: an ordinary division).
+__device__ __forceinline__ int div_index(int n, int d, uint64_t m) {
+  if (m == 0) return n / d;
+  return (int)(((uint64_t)(uint32_t)n * m) >> 32);
+}
+
 // Work item of an attention workgroup: (sequence, kv head, key split, row
 // tile) and its key range.  Static plan: the grid enumerates every group,
 // groups without a selected head exit.  Device plan: the grid enumerates the
@@ -120,11 +126,11 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
   int kps = p.keys_per_split;
   const int int_count = partial ? p.int_count : 0;
   if ((int)blockIdx.x < int_count) {   // a fused step's block-internal item (they come first)
-    int w = xcd_remap(blockIdx.x, int_count);
-    it.rt = w % p.row_tiles;
-    w /= p.row_tiles;
-    it.g = w % p.hkv;
-    it.b = w / p.hkv;
+    const int w = xcd_remap(blockIdx.x, int_count);
+    const int w1 = div_index(w, p.row_tiles, p.dv_row_tiles);
+    it.rt = w - w1 * p.row_tiles;
+    it.b = div_index(w1, p.hkv, p.dv_hkv);
+    it.g = w1 - it.b * p.hkv;
     it.split = p.int_split;
     it.key_begin = 0;
     it.key_end = p.bs;
@@ -154,16 +160,18 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
     kps = ((tiles + splits - 1) / splits) * kKeyTile;
   } else {
     int w = xcd_remap(w0, (int)gridDim.x - int_count);
-    it.rt = w % p.row_tiles;
-    w /= p.row_tiles;
+    int q = div_index(w, p.row_tiles, p.dv_row_tiles);
+    it.rt = w - q * p.row_tiles;
+    w = q;
     if (partial) {
-      it.split = w % p.splits;
-      w /= p.splits;
+      q = div_index(w, p.splits, p.dv_splits);
+      it.split = w - q * p.splits;
+      w = q;
     } else {
       it.split = 0;   // merge launches run one key range per group
     }
-    it.g = w % p.hkv;
-    it.b = w / p.hkv;
+    it.b = div_index(w, p.hkv, p.dv_hkv);
+    it.g = w - it.b * p.hkv;
     it.ok = true;
     if (partial) {
       bool any;

@@ -69,6 +69,10 @@ struct AttnParams {
   int32_t grid;           // workgroups; 0: batch * hkv * splits * row_tiles
   int32_t splits;         // key ranges per group
   int32_t keys_per_split; // multiple of kKeyTile; with a device plan, the longest range it may pick
+  // The work-item decode divides grid indices by row_tiles, splits and hkv:
+  // each as a multiply by ceil(2^32 / d) (div_magic, set at launch; 0 = an
+  // ordinary division).
+  uint64_t dv_row_tiles, dv_splits, dv_hkv;
   int32_t ring_keys;      // longest key range of any item of the launch (LDS ring sizing)
   float scale_log2;       // softmax scale * log2(e)
   HeadSel sel;
@@ -173,5 +177,22 @@ hipError_t launch_decide(const DecideParams& p, hipStream_t s);
 hipError_t launch_reset(const ResetParams& p, hipStream_t s);
 hipError_t launch_complement(const ComplementParams& p, hipStream_t s);
 hipError_t launch_record(const HeadSel& sel, uint8_t* rec, int n_heads, int hq, hipStream_t s);
+
+// ceil(2^32 / d): then n / d = floor(n * m / 2^32) exactly for every n with
+// n * d < 2^32 (the rounding up of m adds less than n / 2^32 < 1 / d).  0
+// (an ordinary division) when some index below n_max breaks that bound.
+inline uint64_t div_magic(int d, long long n_max) {
+  if (d <= 0 || n_max < 0 || (unsigned long long)n_max * (unsigned long long)d >= (1ull << 32)) return 0;
+  return ((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d;
+}
+
+// The decode's divisors for a launch of `blocks` workgroups.
+inline AttnParams with_div_magic(const AttnParams& p, int blocks) {
+  AttnParams q = p;
+  q.dv_row_tiles = div_magic(p.row_tiles, blocks);
+  q.dv_splits = div_magic(p.splits, blocks);
+  q.dv_hkv = div_magic(p.hkv, blocks);
+  return q;
+}
 
 }  // namespace fbk
