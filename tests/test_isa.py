@@ -65,3 +65,37 @@ def test_attention_kernels_do_not_spill(attn_asm):
     assert len(sizes) == len(kernels)
     assert all(int(s) == 0 for s in sizes), list(zip(kernels, sizes))
     assert not any(l.startswith("scratch_") for l in _instructions(attn_asm))
+
+
+DIV_CHECK = r"""
+#include <cstdio>
+#include "fb_internal.h"
+// n / d through div_magic's multiplier, as the work-item decode does it
+static long long via(long long n, uint64_t m) { return (long long)(((uint64_t)(uint32_t)n * m) >> 32); }
+int main() {
+  long bad = 0;
+  for (int d = 1; d <= 5000; ++d) {
+    const long long n_max = ((1LL << 32) - 1) / d;   // every n below keeps n * d < 2^32
+    const uint64_t m = fbk::div_magic(d, n_max);
+    if (m == 0) { ++bad; continue; }
+    for (long long n = 0; n < n_max && n < (1 << 16); ++n) bad += via(n, m) != n / d;
+    for (long long n = n_max - 1; n >= 0 && n > n_max - 4096; --n) bad += via(n, m) != n / d;
+  }
+  bad += fbk::div_magic(3, 1LL << 31) != 0;   // a bound it cannot meet: ordinary division
+  bad += fbk::div_magic(0, 10) != 0;
+  std::printf("%ld\n", bad);
+  return bad != 0;
+}
+"""
+
+
+def test_decode_multiplier_is_exact(tmp_path):
+    """The attention work-item decode replaces n / d by a multiply with
+    div_magic(d) = ceil(2^32 / d): exact for every index n with n d < 2^32."""
+    src, exe = tmp_path / "div_check.cpp", tmp_path / "div_check"
+    src.write_text(DIV_CHECK)
+    r = subprocess.run([B.HIPCC, "-O2", "-std=c++17", "-I", os.path.join(B.ROOT, "include"), "-I", B.CSRC,
+                        str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout + r.stderr
