@@ -560,7 +560,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
           if constexpr (kShortSkip) {
-            if (key0 + 32 * h + 32 <= lim) continue;
+            if (key0 + 32 * h + 32 <= lim || h >= nh_live) continue;   // full, or skipped below
             if (key0 + 32 * h >= lim) {
 #pragma unroll
               for (int j = 0; j < 16; ++j) s[h][j] = -INFINITY;
@@ -579,6 +579,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
         float mx = -INFINITY;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
+          if (kShortSkip && h >= nh_live) continue;   // a half with no key: never exponentiated
 #pragma unroll
           for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[h][j]);
         }
