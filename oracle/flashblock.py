@@ -41,7 +41,10 @@ float64 scaled_dot_product_attention (with its GQA head mapping) and
 logsumexp, and closed forms (single key, constant V, equal keys, a worked
 two-key case); ``merge`` against full attention over the concatenated keys
 (the exact identity the equation implies), the empty-prefix case and split
-associativity; ``cosine`` against scipy and its special values; ``decide`` /
+associativity; ``internal_merge`` against torch's SDPA over the prefix and
+the block together (fresh external part), a scalar brute force with a stale
+external part, and the empty-prefix case; ``cosine`` against scipy and its
+special values; ``decide`` /
 ``run_block`` through the policy closed forms (tau=0, M=0, tau>Bs, gamma>=1,
 gamma=-1, sigma=0).  Parity unpinned: the composition of a whole policy run
 beyond those special cases has no printed values to compare with.
@@ -365,7 +368,10 @@ def external(q: np.ndarray, k_prefix: np.ndarray, v_prefix: np.ndarray, n_prefix
 
 def internal_merge(q: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray, a_out: np.ndarray,
                    l_out: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
-    """Block-internal part for every head, merged with a given external part."""
+    """Block-internal part for every head (§2 "Mécanisme Central": A_in over
+    the block's own tokens J_in, key/value head h // G), merged with a given
+    external part (A_out, L_out) by the A_full equation; the external part may
+    be stale, i.e. computed at an earlier step for other queries."""
     bsz, hq, bs, d = q.shape
     group = hq // k_blk.shape[1]
     scale = default_scale(d) if scale is None else scale

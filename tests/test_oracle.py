@@ -505,11 +505,74 @@ def pin_sparse_gamma_on_residual():
             assert abs(res.sim[1, bi, h] - ref) < 1e-12
 
 
+# ---------------------------------------------------------------- internal_merge
+
+def pin_internal_merge_fresh_is_full_attention():
+    """Block-internal attention merged with a freshly computed external part
+    is attention over the prefix and the block together (the identity the A_full
+    equation implies), for every query head with its grouped key/value head:
+    torch's float64 SDPA with its own GQA mapping over the concatenated keys."""
+    rng = _rng(40)
+    for (b, hq, hkv, bs, n, d) in [(2, 8, 2, 5, 37, 16), (1, 6, 3, 1, 1, 8), (1, 4, 4, 9, 64, 32)]:
+        q = rng.standard_normal((b, hq, bs, d)) * 1.5
+        kp, vp = rng.standard_normal((b, hkv, n + 3, d)) * 1.5, rng.standard_normal((b, hkv, n + 3, d))
+        kb, vb = rng.standard_normal((b, hkv, bs, d)) * 1.5, rng.standard_normal((b, hkv, bs, d))
+        a_out, l_out = fb.external(q, kp, vp, n)
+        out = fb.internal_merge(q, kb, vb, a_out, l_out)
+        kc = torch.from_numpy(np.concatenate([kp[:, :, :n], kb], axis=2)).contiguous()
+        vc = torch.from_numpy(np.concatenate([vp[:, :, :n], vb], axis=2)).contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kc, vc, enable_gqa=True).numpy()
+        assert np.max(np.abs(out - ref)) <= TOL
+
+
+def pin_internal_merge_stale_bruteforce():
+    """With a stale external part (computed for other queries), the output
+    weighs the prefix keys by those queries' scores and the block keys by the
+    current ones: scalar brute force per (sequence, query head), key/value head
+    h // G, on tiny inputs."""
+    rng = _rng(41)
+    b, hq, hkv, bs, n, d = 2, 4, 2, 3, 6, 4
+    q_old = rng.standard_normal((b, hq, bs, d))
+    q = rng.standard_normal((b, hq, bs, d))
+    kp, vp = rng.standard_normal((b, hkv, n, d)), rng.standard_normal((b, hkv, n, d))
+    kb, vb = rng.standard_normal((b, hkv, bs, d)), rng.standard_normal((b, hkv, bs, d))
+    a_old, l_old = fb.external(q_old, kp, vp, n)
+    out = fb.internal_merge(q, kb, vb, a_old, l_old)
+    c = 1.0 / math.sqrt(d)
+    for bi in range(b):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            for i in range(bs):
+                terms = [(q_old[bi, h, i], kp[bi, g, j], vp[bi, g, j]) for j in range(n)]
+                terms += [(q[bi, h, i], kb[bi, g, j], vb[bi, g, j]) for j in range(bs)]
+                num, den = [0.0] * d, 0.0
+                for qi, kj, vj in terms:
+                    w = math.exp(c * sum(float(qi[t]) * float(kj[t]) for t in range(d)))
+                    den += w
+                    num = [num[t] + w * float(vj[t]) for t in range(d)]
+                assert np.max(np.abs(out[bi, h, i] - np.array(num) / den)) < 1e-12
+
+
+def pin_internal_merge_empty_external():
+    """An empty external part (no prefix: A = 0, L = -inf) leaves the block's
+    own attention: torch SDPA over the block keys alone."""
+    rng = _rng(42)
+    b, hq, hkv, bs, d = 1, 6, 2, 7, 16
+    q = rng.standard_normal((b, hq, bs, d))
+    kb, vb = rng.standard_normal((b, hkv, bs, d)), rng.standard_normal((b, hkv, bs, d))
+    out = fb.internal_merge(q, kb, vb, np.zeros((b, hq, bs, d)), np.full((b, hq, bs), -np.inf))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(kb), torch.from_numpy(vb), enable_gqa=True).numpy()
+    assert np.max(np.abs(out - ref)) <= TOL
+
+
 PINS = [pin_attend_bruteforce, pin_attend_vs_torch, pin_external_gqa_vs_torch, pin_attend_closed_forms,
         pin_attend_permutation_invariance, pin_merge_equals_full_attention, pin_merge_special_cases,
         pin_split_associativity, pin_cosine, pin_tau_policy, pin_gamma_policy, pin_multi_block_append,
         pin_tau_cum_policy, pin_gamma_group_policy, pin_sparse_always_is_exact, pin_sparse_all_kept_is_exact,
-        pin_sparse_none_kept_is_flashblock, pin_sparse_stale_residual_bruteforce, pin_sparse_gamma_on_residual]
+        pin_sparse_none_kept_is_flashblock, pin_sparse_stale_residual_bruteforce, pin_sparse_gamma_on_residual,
+        pin_internal_merge_fresh_is_full_attention, pin_internal_merge_stale_bruteforce,
+        pin_internal_merge_empty_external]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -635,6 +698,30 @@ def _sparse_sets_whole_prefix_left(tiles, n_prefix):
     return fb.tile_rows(tiles, n_prefix), np.arange(n_prefix)
 
 
+def _internal_merge_mod_group(q, k_blk, v_blk, a_out, l_out, scale=None):
+    # query head h reads block key/value head h % Hkv instead of h // G
+    bsz, hq, bs, d = q.shape
+    hkv = k_blk.shape[1]
+    out = np.empty((bsz, hq, bs, d))
+    for b in range(bsz):
+        for h in range(hq):
+            a_in, l_in = _real_attend(q[b, h], k_blk[b, h % hkv], v_blk[b, h % hkv], fb.default_scale(d))
+            out[b, h], _ = _real_merge(a_out[b, h], l_out[b, h], a_in, l_in)
+    return out
+
+
+def _internal_merge_swapped_l(q, k_blk, v_blk, a_out, l_out, scale=None):
+    # each part weighted with the other part's normaliser
+    bsz, hq, bs, d = q.shape
+    group = hq // k_blk.shape[1]
+    out = np.empty((bsz, hq, bs, d))
+    for b in range(bsz):
+        for h in range(hq):
+            a_in, l_in = _real_attend(q[b, h], k_blk[b, h // group], v_blk[b, h // group], fb.default_scale(d))
+            out[b, h], _ = _real_merge(a_out[b, h], l_in, a_in, l_out[b, h])
+    return out
+
+
 MUTANTS = [
     ("attend", _attend_no_max_shift), ("attend", _attend_log2), ("attend", _attend_no_scale),
     ("attend", _attend_kv_swapped), ("attend", _attend_unnormalised),
@@ -645,6 +732,7 @@ MUTANTS = [
     ("external", _external_mod_group),
     ("sparse_key_sets", _sparse_sets_shifted), ("sparse_key_sets", _sparse_sets_no_residual),
     ("sparse_key_sets", _sparse_sets_whole_prefix_left),
+    ("internal_merge", _internal_merge_mod_group), ("internal_merge", _internal_merge_swapped_l),
 ]
 
 
