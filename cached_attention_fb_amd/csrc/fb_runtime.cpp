@@ -62,6 +62,7 @@ struct ProfRec {
 
 struct fb_cache {
   fb_config cfg{};
+  int kv_splits = 0;     // 0: automatic; else forced prefix chunks (fb_cache_opts)
   int device = 0;
   int group = 1;         // Hq / Hkv
   int rows = 0;          // packed rows per (b, kv head) = group * Bs
@@ -100,6 +101,7 @@ struct fb_cache {
   int comp_stride = 1;       // ceil(max_prefix / 64), at least 1
   // host state
   int64_t steps = 0;         // fb_step calls since the last reset
+  bool ext_since_reset = false;   // fb_external_attn filled the cache since the last reset
   int32_t block_prefix = -1; // prefix_len of the current block
   int32_t block_policy = -1;
   int32_t block_dev_m = -1;  // 1: the block's threshold decisions are made on the device
@@ -130,8 +132,6 @@ fb_status check_config(const fb_config* cfg) {
     return fail(FB_E_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", cfg->n_q_heads, cfg->n_kv_heads);
   if (cfg->block_size < 1 || cfg->block_size > (1 << 20)) return fail(FB_E_SHAPE, "block_size %d invalid", cfg->block_size);
   if (cfg->max_prefix < 0) return fail(FB_E_SHAPE, "max_prefix %d is negative", cfg->max_prefix);
-  if (cfg->kv_splits < 0 || cfg->kv_splits > fbk::kMaxSplits)
-    return fail(FB_E_ARG, "kv_splits %d outside [0, %d]", cfg->kv_splits, fbk::kMaxSplits);
   if (!(cfg->softmax_scale == cfg->softmax_scale) || std::isinf(cfg->softmax_scale))
     return fail(FB_E_ARG, "softmax_scale is not finite");
   if (cfg->head_dim != 64 && cfg->head_dim != 128)
@@ -181,8 +181,8 @@ int choose_splits(fb_cache* c, int n_keys, int active_groups, int co_items = 0, 
   const int tiles = (n_keys + fbk::kKeyTile - 1) / fbk::kKeyTile;
   if (tiles <= 1) return 1;
   int want;
-  if (c->cfg.kv_splits > 0) {
-    want = c->cfg.kv_splits;
+  if (c->kv_splits > 0) {
+    want = c->kv_splits;
   } else {
     const auto key = std::make_tuple(n_keys, active_groups, co_items, co_tiles);
     const auto hit = c->split_memo.find(key);
@@ -474,6 +474,7 @@ fb_status run_reset(fb_cache* c, hipStream_t s) {
   prof_end(c, s, &r);
   if (e != hipSuccess) return hip_fail(e, "reset launch");
   c->steps = 0;
+  c->ext_since_reset = false;
   c->block_prefix = -1;
   c->block_policy = -1;
   c->block_dev_m = -1;
@@ -500,10 +501,27 @@ extern "C" {
 
 const char* fb_last_error(void) { return g_err.c_str(); }
 
-fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
+}  // extern "C"
+
+namespace {
+
+// Copies a caller's options struct that starts with its own size: the bytes
+// the caller has (at most sizeof(T)); fields past them keep T's defaults.
+template <typename T>
+fb_status read_opts(const T* in, T* out, const char* what) {
+  *out = T{};
+  if (!in) return FB_OK;
+  if (in->struct_size < sizeof(uint32_t)) return fail(FB_E_ARG, "%s.struct_size %u is too small", what, in->struct_size);
+  std::memcpy(out, in, std::min<size_t>(in->struct_size, sizeof(T)));
+  return FB_OK;
+}
+
+fb_status alloc_impl(const fb_config* cfg, int kv_splits, fb_cache** out) {
   if (!out) return fail(FB_E_ARG, "out is null");
   fb_status st = check_config(cfg);
   if (st != FB_OK) return st;
+  if (kv_splits < 0 || kv_splits > fbk::kMaxSplits)
+    return fail(FB_E_ARG, "kv_splits %d outside [0, %d]", kv_splits, fbk::kMaxSplits);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "no usable HIP device");
@@ -514,6 +532,7 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
   fb_cache* c = new (std::nothrow) fb_cache();
   if (!c) return fail(FB_E_NOMEM, "host allocation failed");
   c->cfg = *cfg;
+  c->kv_splits = kv_splits;
   c->device = dev;
   c->group = cfg->n_q_heads / cfg->n_kv_heads;
   c->rows = c->group * cfg->block_size;
@@ -550,7 +569,7 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
         cap = std::max(cap, std::min(kDynSplitCap, choose_splits(c, cfg->max_prefix, n)));
     c->splits_cap = cap;
   }
-  if (cfg->kv_splits > 0) c->splits_cap = std::max(c->splits_cap, std::min(cfg->kv_splits, fbk::kMaxSplits));
+  if (kv_splits > 0) c->splits_cap = std::max(c->splits_cap, std::min(kv_splits, fbk::kMaxSplits));
   c->split_memo.clear();   // those choices were made before the cap was known
 
   c->comp_stride = std::max(1, (cfg->max_prefix + fbk::kKeyTile - 1) / fbk::kKeyTile);
@@ -597,6 +616,18 @@ fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) {
   return ok();
 }
 
+}  // namespace
+
+extern "C" {
+
+fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out) { return alloc_impl(cfg, 0, out); }
+
+fb_status fb_cache_alloc_ex(const fb_config* cfg, const fb_cache_opts* opts, fb_cache** out) {
+  fb_cache_opts o;
+  if (fb_status st = read_opts(opts, &o, "fb_cache_opts"); st != FB_OK) return st;
+  return alloc_impl(cfg, o.kv_splits, out);
+}
+
 fb_status fb_cache_free(fb_cache* c) {
   if (!c) return ok();
   DeviceGuard g(c->device);
@@ -631,6 +662,7 @@ fb_status fb_external_attn(fb_cache* c, const void* q_blk, const void* k_prefix,
                               c->cfg.batch * c->cfg.n_kv_heads, (hipStream_t)stream, ExtOpts{});
   if (st != FB_OK) return st;
   std::fill(c->host_valid.begin(), c->host_valid.end(), head_mask ? 0 : 1);
+  c->ext_since_reset = true;
   return ok();
 }
 
@@ -659,11 +691,14 @@ struct SparseSel {
 // prefix tiles the selection leaves out (their list is built at the block's
 // first step), and the kept tiles are attended afresh for every head at every
 // step and folded with it into the total buffer that the merge reads.
-fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, const void* k_blk,
-                    const void* v_blk, const void* k_prefix, const void* v_prefix, int32_t prefix_len,
-                    const SparseSel* sp, void* out, void* stream) {
+fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const fb_step_opts* opts_in, const void* q_blk,
+                    const void* k_blk, const void* v_blk, const void* k_prefix, const void* v_prefix,
+                    int32_t prefix_len, const SparseSel* sp, void* out, void* stream) {
   if (!c) return fail(FB_E_ARG, "cache is null");
   if (!pa) return fail(FB_E_ARG, "policy args are null");
+  fb_step_opts opts;
+  if (fb_status ost = read_opts(opts_in, &opts, "fb_step_opts"); ost != FB_OK) return ost;
+  const int32_t* const n_updated_dev = opts.n_updated_dev;
   if (!q_blk || !k_blk || !v_blk || !out) return fail(FB_E_ARG, "a tensor pointer is null");
   if (pa->policy != FB_POLICY_ALWAYS && pa->policy != FB_POLICY_TAU && pa->policy != FB_POLICY_GAMMA &&
       pa->policy != FB_POLICY_TAU_CUM && pa->policy != FB_POLICY_GAMMA_GROUP)
@@ -688,11 +723,11 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
   if (c->steps > 0 && n_sel != c->block_n_sel)
     return fail(FB_E_STATE, "the sparse selection (or its absence) changed inside a block (reset first)");
   const int B = c->cfg.batch;
-  const bool dev_m = tau_like && pa->n_updated_dev != nullptr;
+  const bool dev_m = tau_like && n_updated_dev != nullptr;
   if (tau_like) {
     if (pa->tau < 0) return fail(FB_E_ARG, "tau %d is negative", pa->tau);
-    if (!pa->n_updated && !pa->n_updated_dev) return fail(FB_E_ARG, "n_updated and n_updated_dev are null under the tau policy");
-    if (pa->n_updated && pa->n_updated_dev) return fail(FB_E_ARG, "both n_updated and n_updated_dev are set");
+    if (!pa->n_updated && !n_updated_dev) return fail(FB_E_ARG, "n_updated is null under the tau policy");
+    if (pa->n_updated && n_updated_dev) return fail(FB_E_ARG, "both n_updated and n_updated_dev are set");
     if (!dev_m)
       for (int b = 0; b < B; ++b)
         if (pa->n_updated[b] < 0) return fail(FB_E_ARG, "n_updated[%d] = %d is negative", b, pa->n_updated[b]);
@@ -706,8 +741,9 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
   std::vector<uint8_t> reuse_seq(B, 0);
   for (int b = 0; b < B && !dev_m; ++b) {
     bool reuse = false;
-    if (pa->policy == FB_POLICY_TAU) reuse = c->host_valid[b] && pa->n_updated[b] < pa->tau;
-    if (pa->policy == FB_POLICY_TAU_CUM) reuse = c->host_valid[b] && c->cum_updated[b] + pa->n_updated[b] < pa->tau;
+    const bool has = c->steps > 0 && c->host_valid[b];   // the first step of a block recomputes
+    if (pa->policy == FB_POLICY_TAU) reuse = has && pa->n_updated[b] < pa->tau;
+    if (pa->policy == FB_POLICY_TAU_CUM) reuse = has && c->cum_updated[b] + pa->n_updated[b] < pa->tau;
     reuse_seq[b] = reuse ? 1 : 0;
     if (!reuse) {
       sel.seq_bits[b >> 5] |= 1u << (b & 31);
@@ -719,6 +755,12 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
   if (g.err != hipSuccess) return hip_fail(g.err, "set device");
   hipStream_t s = (hipStream_t)stream;
   if (fb_status pst = check_not_capturing_profiled(c, s); pst != FB_OK) return pst;
+  if (c->steps == 0 && c->ext_since_reset) {
+    // fb_external_attn filled the cache after the reset: empty it again, so
+    // that the device-side flags (valid, similarity) make this first step
+    // recompute every head as the host's decisions above do
+    if (fb_status rst = run_reset(c, s); rst != FB_OK) return rst;
+  }
   const int64_t nh = (int64_t)B * c->cfg.n_q_heads;
   uint8_t* reuse_now = c->reuse + (c->steps & 1) * nh;
   uint8_t* reuse_next = c->reuse + ((c->steps + 1) & 1) * nh;
@@ -761,13 +803,13 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const void* q_blk, co
     // threshold decided in the attention launch from the counts in device
     // memory; it records the decisions, the combine follows them
     ext_sel = all_heads(c);
-    ext_sel.m = pa->n_updated_dev;
+    ext_sel.m = n_updated_dev;
     ext_sel.tau = pa->tau;
     ext_sel.valid = c->valid;
     ext_sel.cum = pa->policy == FB_POLICY_TAU_CUM ? c->cum : nullptr;
     ext_active = groups;
     eo.rec = reuse_now;
-    if (pa->policy == FB_POLICY_TAU_CUM) eo.cum_m = pa->n_updated_dev;
+    if (pa->policy == FB_POLICY_TAU_CUM) eo.cum_m = n_updated_dev;
   } else {
     ext_sel.flags = nullptr;
     ext_sel.flags_select = 1;
@@ -851,14 +893,20 @@ extern "C" {
 fb_status fb_step(fb_cache* c, const fb_policy_args* pa, const void* q_blk, const void* k_blk,
                   const void* v_blk, const void* k_prefix, const void* v_prefix, int32_t prefix_len,
                   void* out, void* stream) {
-  return step_impl(c, pa, q_blk, k_blk, v_blk, k_prefix, v_prefix, prefix_len, nullptr, out, stream);
+  return step_impl(c, pa, nullptr, q_blk, k_blk, v_blk, k_prefix, v_prefix, prefix_len, nullptr, out, stream);
 }
 
-fb_status fb_step_sparse(fb_cache* c, const fb_policy_args* pa, const void* q_blk, const void* k_blk,
-                         const void* v_blk, const void* k_prefix, const void* v_prefix, int32_t prefix_len,
-                         const int32_t* sel_tiles, int32_t n_sel, void* out, void* stream) {
+fb_status fb_step_ex(fb_cache* c, const fb_policy_args* pa, const fb_step_opts* opts, const void* q_blk,
+                     const void* k_blk, const void* v_blk, const void* k_prefix, const void* v_prefix,
+                     int32_t prefix_len, void* out, void* stream) {
+  return step_impl(c, pa, opts, q_blk, k_blk, v_blk, k_prefix, v_prefix, prefix_len, nullptr, out, stream);
+}
+
+fb_status fb_step_sparse(fb_cache* c, const fb_policy_args* pa, const fb_step_opts* opts, const void* q_blk,
+                         const void* k_blk, const void* v_blk, const void* k_prefix, const void* v_prefix,
+                         int32_t prefix_len, const int32_t* sel_tiles, int32_t n_sel, void* out, void* stream) {
   const SparseSel sp{sel_tiles, n_sel};
-  return step_impl(c, pa, q_blk, k_blk, v_blk, k_prefix, v_prefix, prefix_len, &sp, out, stream);
+  return step_impl(c, pa, opts, q_blk, k_blk, v_blk, k_prefix, v_prefix, prefix_len, &sp, out, stream);
 }
 
 fb_status fb_cache_read(const fb_cache* c, int32_t field, void* host_dst, size_t bytes, void* stream) {

@@ -27,20 +27,32 @@ KIND_NAMES = ["external", "combine", "internal_merge", "decide", "reset", "spars
 STATUS_NAMES = {0: "FB_OK", 1: "FB_E_ARG", 2: "FB_E_SHAPE", 3: "FB_E_DTYPE", 4: "FB_E_STATE",
                 5: "FB_E_NOMEM", 6: "FB_E_HIP", 7: "FB_E_UNSUPPORTED"}
 
-EXPORTED = ["fb_cache_alloc", "fb_cache_free", "fb_cache_reset", "fb_external_attn",
-            "fb_internal_attn_merge", "fb_step", "fb_step_sparse", "fb_cache_read", "fb_cache_info",
-            "fb_profile_enable", "fb_profile_read", "fb_last_error"]
+EXPORTED = ["fb_cache_alloc", "fb_cache_alloc_ex", "fb_cache_free", "fb_cache_reset", "fb_external_attn",
+            "fb_internal_attn_merge", "fb_step", "fb_step_ex", "fb_step_sparse", "fb_cache_read",
+            "fb_cache_info", "fb_profile_enable", "fb_profile_read", "fb_last_error"]
 
 
 class FBConfig(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("max_prefix", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("kv_splits", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class FBCacheOpts(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("kv_splits", ctypes.c_int32)]
 
 
 class FBPolicyArgs(ctypes.Structure):
     _fields_ = [("policy", ctypes.c_int32), ("tau", ctypes.c_int32), ("gamma", ctypes.c_float),
-                ("n_updated", ctypes.POINTER(ctypes.c_int32)), ("n_updated_dev", ctypes.c_void_p)]
+                ("n_updated", ctypes.POINTER(ctypes.c_int32))]
+
+
+class FBStepOpts(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("n_updated_dev", ctypes.c_void_p)]
+
+
+def step_opts(n_updated_dev: Optional[int]) -> FBStepOpts:
+    return FBStepOpts(ctypes.sizeof(FBStepOpts), n_updated_dev)
 
 
 class FBProfileStats(ctypes.Structure):
@@ -66,12 +78,16 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32
     lib.fb_cache_alloc.argtypes = [ctypes.POINTER(FBConfig), ctypes.POINTER(vp)]
+    lib.fb_cache_alloc_ex.argtypes = [ctypes.POINTER(FBConfig), ctypes.POINTER(FBCacheOpts), ctypes.POINTER(vp)]
     lib.fb_cache_free.argtypes = [vp]
     lib.fb_cache_reset.argtypes = [vp, vp]
     lib.fb_external_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp]
     lib.fb_internal_attn_merge.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.fb_step.argtypes = [vp, ctypes.POINTER(FBPolicyArgs), vp, vp, vp, vp, vp, i32, vp, vp]
-    lib.fb_step_sparse.argtypes = [vp, ctypes.POINTER(FBPolicyArgs), vp, vp, vp, vp, vp, i32, vp, i32, vp, vp]
+    lib.fb_step_ex.argtypes = [vp, ctypes.POINTER(FBPolicyArgs), ctypes.POINTER(FBStepOpts), vp, vp, vp, vp, vp, i32,
+                               vp, vp]
+    lib.fb_step_sparse.argtypes = [vp, ctypes.POINTER(FBPolicyArgs), ctypes.POINTER(FBStepOpts), vp, vp, vp, vp, vp,
+                                   i32, vp, i32, vp, vp]
     lib.fb_cache_read.argtypes = [vp, i32, vp, ctypes.c_size_t, vp]
     lib.fb_cache_info.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32)]
     lib.fb_profile_enable.argtypes = [vp, i32]
@@ -108,9 +124,13 @@ class Cache:
         self.dtype = dtype
         self.cfg = FBConfig(batch, n_q_heads, n_kv_heads, head_dim, block_size, max_prefix,
                             FB_F32 if dtype == torch.float32 else FB_BF16 if dtype == torch.bfloat16 else -1,
-                            softmax_scale, kv_splits)
+                            softmax_scale)
         h = ctypes.c_void_p()
-        _check(self.lib.fb_cache_alloc(ctypes.byref(self.cfg), ctypes.byref(h)))
+        if kv_splits:
+            opts = FBCacheOpts(ctypes.sizeof(FBCacheOpts), kv_splits)
+            _check(self.lib.fb_cache_alloc_ex(ctypes.byref(self.cfg), ctypes.byref(opts), ctypes.byref(h)))
+        else:
+            _check(self.lib.fb_cache_alloc(ctypes.byref(self.cfg), ctypes.byref(h)))
         self.h = h
 
     # -- shape checks (marshalling only) --------------------------------
@@ -167,14 +187,15 @@ class Cache:
         decisions are made on the device.  `sel_tiles` (int32 device tensor
         [B, Hkv, n_sel]): a sparse attention's kept prefix tiles
         (fb_step_sparse)."""
-        args = FBPolicyArgs(policy, tau, gamma, None, None)
+        args = FBPolicyArgs(policy, tau, gamma, None)
+        opts = None
         keep = None
         if n_updated_dev is not None:
             if (not isinstance(n_updated_dev, torch.Tensor) or n_updated_dev.dtype != torch.int32
                     or not n_updated_dev.is_cuda or n_updated_dev.numel() != self.cfg.batch
                     or not n_updated_dev.is_contiguous()):
                 raise ValueError(f"n_updated_dev must be a contiguous int32 device tensor of {self.cfg.batch} entries")
-            args.n_updated_dev = n_updated_dev.data_ptr()
+            opts = step_opts(n_updated_dev.data_ptr())
         if n_updated is not None:
             keep = np.ascontiguousarray(np.asarray(n_updated, dtype=np.int32).reshape(-1))
             if keep.size != self.cfg.batch:
@@ -182,15 +203,19 @@ class Cache:
             args.n_updated = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         if sel_tiles is not None:
             sel_ptr, n_sel = self._sel(sel_tiles)
-            _check(self.lib.fb_step_sparse(self.h, ctypes.byref(args), self._q(q), self._kv_blk(k_blk, "k_blk"),
+            _check(self.lib.fb_step_sparse(self.h, ctypes.byref(args), None if opts is None else ctypes.byref(opts),
+                                           self._q(q), self._kv_blk(k_blk, "k_blk"),
                                            self._kv_blk(v_blk, "v_blk"), self._kv_pre(k_prefix, "k_prefix"),
                                            self._kv_pre(v_prefix, "v_prefix"), int(prefix_len), sel_ptr, n_sel,
                                            self._q(out, "out"), _stream(stream)))
             return
-        _check(self.lib.fb_step(self.h, ctypes.byref(args), self._q(q), self._kv_blk(k_blk, "k_blk"),
-                                self._kv_blk(v_blk, "v_blk"), self._kv_pre(k_prefix, "k_prefix"),
-                                self._kv_pre(v_prefix, "v_prefix"), int(prefix_len), self._q(out, "out"),
-                                _stream(stream)))
+        ptrs = (self._q(q), self._kv_blk(k_blk, "k_blk"), self._kv_blk(v_blk, "v_blk"),
+                self._kv_pre(k_prefix, "k_prefix"), self._kv_pre(v_prefix, "v_prefix"), int(prefix_len),
+                self._q(out, "out"), _stream(stream))
+        if opts is not None:
+            _check(self.lib.fb_step_ex(self.h, ctypes.byref(args), ctypes.byref(opts), *ptrs))
+        else:
+            _check(self.lib.fb_step(self.h, ctypes.byref(args), *ptrs))
 
     def _sel(self, t: torch.Tensor):
         c = self.cfg
@@ -255,8 +280,10 @@ class PreparedStep:
         self.out = out
         self.m = (ctypes.c_int32 * cache.cfg.batch)()
         self.m_ptr = ctypes.cast(self.m, ctypes.POINTER(ctypes.c_int32))
-        self.args = FBPolicyArgs(0, 0, 0.0, self.m_ptr, None)
+        self.args = FBPolicyArgs(0, 0, 0.0, self.m_ptr)
         self.args_ref = ctypes.byref(self.args)
+        self.opts = step_opts(None)
+        self.opts_ref = ctypes.byref(self.opts)
         self.fn = cache.lib.fb_step
 
     def __call__(self, policy: int, prefix_len: int, n_updated=None, tau: int = 0, gamma: float = 0.0,
@@ -265,20 +292,24 @@ class PreparedStep:
         device); n_updated is then ignored."""
         a = self.args
         a.policy, a.tau, a.gamma = policy, tau, gamma
+        opts = None
         if n_updated_dev is not None:
             a.n_updated = None
-            a.n_updated_dev = n_updated_dev
+            self.opts.n_updated_dev = n_updated_dev
+            opts = self.opts_ref
         else:
             a.n_updated = self.m_ptr
-            a.n_updated_dev = None
             if n_updated is not None:
                 for i, v in enumerate(n_updated):
                     self.m[i] = int(v)
         q, kb, vb, kp, vp = self.ptrs
         st = _stream(stream) if stream is None or not isinstance(stream, int) else stream
         if self.sel is not None:
-            code = self.cache.lib.fb_step_sparse(self.cache.h, self.args_ref, q, kb, vb, kp, vp, prefix_len,
+            code = self.cache.lib.fb_step_sparse(self.cache.h, self.args_ref, opts, q, kb, vb, kp, vp, prefix_len,
                                                  self.sel[0], self.sel[1], self.out, st)
+        elif opts is not None:
+            code = self.cache.lib.fb_step_ex(self.cache.h, self.args_ref, opts, q, kb, vb, kp, vp, prefix_len,
+                                             self.out, st)
         else:
             code = self.fn(self.cache.h, self.args_ref, q, kb, vb, kp, vp, prefix_len, self.out, st)
         if code != FB_OK:

@@ -94,8 +94,15 @@ typedef struct {
   int32_t max_prefix;     /* >= 0: row capacity of the caller's prefix K/V buffers */
   int32_t dtype;          /* FB_F32 | FB_BF16: dtype of Q/K/V and of the output */
   float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim) */
-  int32_t kv_splits;      /* 0: automatic; else number of prefix chunks per (b, kv head) */
 } fb_config;
+
+/* Options of fb_cache_alloc_ex beyond fb_config (tuning and tests).  The
+ * struct may grow: struct_size = sizeof(fb_cache_opts) as the caller was
+ * built; fields past struct_size take their defaults (0). */
+typedef struct {
+  uint32_t struct_size;
+  int32_t kv_splits;      /* 0: automatic; else prefix chunks per (b, kv head), 1..64 */
+} fb_cache_opts;
 
 typedef struct fb_cache fb_cache;   /* opaque; owns device memory (hipMalloc) */
 
@@ -105,10 +112,18 @@ typedef struct fb_cache fb_cache;   /* opaque; owns device memory (hipMalloc) */
  * replaced), per-head flags, scratch for split-prefix partial results sized
  * for max_prefix, and for sparse steps a total buffer of the A_out size and
  * the list of left-out prefix tiles.  The new cache is in the reset state.
- * *out is set only on FB_OK.
+ * The cache holds what page "Résumé Technique : FlashBlock", §2 "Mécanisme
+ * Central", says FlashBlock keeps from one diffusion step to the next: the
+ * block-external output A_out and its log-normaliser L_out = log Z_out.
+ * *out is set only on FB_OK.  The caller frees it with fb_cache_free.
  * Errors: FB_E_ARG (null), FB_E_DTYPE, FB_E_SHAPE, FB_E_UNSUPPORTED,
  * FB_E_NOMEM, FB_E_HIP (no device). */
 fb_status fb_cache_alloc(const fb_config* cfg, fb_cache** out);
+
+/* fb_cache_alloc with options (opts NULL: the defaults).  Errors: those of
+ * fb_cache_alloc, FB_E_ARG (struct_size below 4, kv_splits outside
+ * [0, 64]). */
+fb_status fb_cache_alloc_ex(const fb_config* cfg, const fb_cache_opts* opts, fb_cache** out);
 
 /* Release the cache's device memory after waiting for its device to finish
  * all work.  NULL is a no-op. */
@@ -125,6 +140,8 @@ fb_status fb_cache_reset(fb_cache* c, void* stream);
  * compute A_out (softmax attention of the block queries over prefix rows
  * 0..prefix_len-1, no mask) and L_out, store them as the head's cached pair,
  * and mark the head valid.  prefix_len == 0 stores A_out = 0, L_out = -inf.
+ * What it stores serves fb_internal_attn_merge; fb_step recomputes every head
+ * at the first step of a block whatever the cache holds.
  * Errors: FB_E_ARG, FB_E_SHAPE (prefix_len < 0 or > max_prefix). */
 fb_status fb_external_attn(fb_cache* c, const void* q_blk, const void* k_prefix,
                            const void* v_prefix, int32_t prefix_len,
@@ -149,14 +166,21 @@ typedef struct {
                                 group's similarity */
   const int32_t* n_updated;  /* host int32 [B]: tokens of the block updated since the
                                 previous step (TAU, TAU_CUM; ignored otherwise) */
+} fb_policy_args;
+
+/* Options of fb_step_ex / fb_step_sparse.  The struct may grow: struct_size =
+ * sizeof(fb_step_opts) as the caller was built; fields past struct_size take
+ * their defaults (NULL). */
+typedef struct {
+  uint32_t struct_size;
   const int32_t* n_updated_dev;
-                             /* device int32 [B], values >= 0 (not checked): the same
+                             /* device int32 [B], values >= 0 (not checked): the threshold
                                 counts in device memory, read by the step's kernels when
                                 they run; the decisions are then made on the device, per
-                                head, from each head's own valid flag.  Exactly one of
-                                n_updated and n_updated_dev is set under TAU/TAU_CUM; a
-                                block keeps the same choice until its reset. */
-} fb_policy_args;
+                                head, from each head's own valid flag.  Under TAU/TAU_CUM
+                                exactly one of fb_policy_args.n_updated and n_updated_dev
+                                is set; a block keeps the same choice until its reset. */
+} fb_step_opts;
 
 /* One denoising step (page §2): decide per head whether to reuse the cached
  * A_out/L_out; recompute block-external attention for the other heads and
@@ -165,16 +189,18 @@ typedef struct {
  * decide its reuse at the next step; compute block-internal attention and the
  * merge into `out`.  The first step after a reset recomputes every head, and
  * under GAMMA so does the second (a similarity needs two computed A_out).
+ * The first step after a reset recomputes every head even when
+ * fb_external_attn filled the cache since the reset.
  * The whole step is asynchronous on `stream` (GAMMA decisions and TAU
- * decisions from n_updated_dev stay on the device).  Errors: FB_E_ARG (null,
- * bad policy, tau < 0, neither or both of n_updated / n_updated_dev under TAU,
- * a negative n_updated), FB_E_SHAPE, FB_E_STATE (prefix_len, policy or the
- * host/device choice differs from the previous step of the same block).
+ * decisions from device counts stay on the device).  Errors: FB_E_ARG (null,
+ * bad policy, tau < 0, n_updated null under TAU, a negative n_updated),
+ * FB_E_SHAPE, FB_E_STATE (prefix_len, policy or the host/device choice
+ * differs from the previous step of the same block).
  *
  * Graph capture: fb_step and fb_cache_reset enqueue kernel launches only (no
  * copy, memset, allocation or synchronisation) and, when no decision is made
- * on the host (ALWAYS, GAMMA, GAMMA_GROUP, or TAU/TAU_CUM with
- * n_updated_dev), nothing they enqueue depends on device values read by the
+ * on the host (ALWAYS, GAMMA, GAMMA_GROUP, or TAU/TAU_CUM with device counts
+ * through fb_step_ex), nothing they enqueue depends on device values read by the
  * host, so they may be recorded by HIP stream capture with profiling off.  A
  * replay repeats the launches as recorded, host choices included (the step's
  * position in its block, prefix_len, pointers such as n_updated_dev), so a
@@ -186,6 +212,14 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* p, const void* q_blk, const
                   const void* v_blk, const void* k_prefix, const void* v_prefix,
                   int32_t prefix_len, void* out, void* stream);
 
+/* fb_step with options (opts NULL: fb_step itself): with opts->n_updated_dev
+ * set, the threshold counts are read from device memory and the decisions
+ * made on the device (fb_policy_args.n_updated must then be NULL).  Errors:
+ * those of fb_step, FB_E_ARG (struct_size below 4, both counts set). */
+fb_status fb_step_ex(fb_cache* c, const fb_policy_args* p, const fb_step_opts* opts, const void* q_blk,
+                     const void* k_blk, const void* v_blk, const void* k_prefix, const void* v_prefix,
+                     int32_t prefix_len, void* out, void* stream);
+
 /* One denoising step over a sparse attention (page §2, compatibility with
  * sparse attention; §3, synergy with sparsity): a sparse selection keeps some
  * 64-key tiles of the prefix; the tiles it leaves out are treated as the
@@ -194,26 +228,30 @@ fb_status fb_step(fb_cache* c, const fb_policy_args* p, const void* q_blk, const
  * are attended afresh for every head at every step.  The output is the
  * log-space merge of the cached part, the kept part and the block-internal
  * part.  With every head recomputing (ALWAYS) it is exact attention over the
- * prefix and the block, whatever the selection.
+ * prefix and the block, for every selection that keeps the rule above.
  *   sel_tiles  device int32 [B][Hkv][n_sel]: for each (sequence, kv head), the
  *              kept tiles (tile t = prefix rows 64t .. 64t+63, cut at
- *              prefix_len), distinct, ascending by convention; shared by the
- *              query heads of the kv head.  Entries outside [0, ceil(prefix_len
- *              / 64)) keep nothing.  Read at the block's first step (which
- *              lists the tiles left out) and at every step (kept tiles): the
+ *              prefix_len), shared by the query heads of the kv head.  The
+ *              entries of a (sequence, kv head) must be distinct tiles in
+ *              [0, ceil(prefix_len / 64)) (ascending by convention): the
+ *              library does not read device data back to check, and for any
+ *              other selection the results are unspecified (every access
+ *              stays in bounds).  Read at the block's first step (which lists
+ *              the tiles left out) and at every step (kept tiles): the
  *              selection must stay the same within a block.
  *   n_sel      0 <= n_sel <= ceil(prefix_len / 64), the same for every step of
  *              a block.
+ *   opts       NULL, or as for fb_step_ex (device counts).
  * Under GAMMA the similarity is that of the cached (left-out) part.  The
  * cache fields A_out/L_out hold the left-out keys' part.  Policies, counts,
  * graph capture and asynchrony are as for fb_step; a block is either dense
  * (fb_step) or sparse (fb_step_sparse) until its reset.  Errors: those of
  * fb_step, FB_E_ARG (sel_tiles null with n_sel > 0), FB_E_SHAPE (n_sel out of
  * range), FB_E_STATE (n_sel, or sparse vs dense, changed inside a block). */
-fb_status fb_step_sparse(fb_cache* c, const fb_policy_args* p, const void* q_blk, const void* k_blk,
-                         const void* v_blk, const void* k_prefix, const void* v_prefix,
-                         int32_t prefix_len, const int32_t* sel_tiles, int32_t n_sel, void* out,
-                         void* stream);
+fb_status fb_step_sparse(fb_cache* c, const fb_policy_args* p, const fb_step_opts* opts,
+                         const void* q_blk, const void* k_blk, const void* v_blk,
+                         const void* k_prefix, const void* v_prefix, int32_t prefix_len,
+                         const int32_t* sel_tiles, int32_t n_sel, void* out, void* stream);
 
 /* Copy one field of the cache (layouts in the FB_FIELD_* list) to host
  * memory `host_dst` of exactly `bytes` bytes, after the work already on
