@@ -20,6 +20,7 @@
 //   K: chunk c of key k at c ^ (k % (D/8))       (16 rows, one chunk column: all banks)
 //   V: chunk c of key k at c ^ (4(k % 4) % (D/8)) (4 rows x 64 B of a transposed read: all banks)
 #include <algorithm>
+#include <atomic>
 
 #include "fb_device.h"
 
@@ -714,12 +715,17 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   constexpr int kMaxLds = std::max({P::kLdsBytes, P::q_offset(P::kStages, ROWW) + kQBytes,
                                     (P::kStages - 1) * P::kStageBytes + kQBytes,
                                     KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
-  static bool attr_set = false;
-  if (!attr_set) {
+  // The LDS limit is raised once per device (a bit per device id below 64;
+  // others set it at every launch).  Two threads may both set it: harmless.
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (bit == 0 || (attr_done.load(std::memory_order_acquire) & bit) == 0) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX, ONE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_done.fetch_or(bit, std::memory_order_release);
   }
   // a workgroup never uses more ring stages than its key range has tiles
   const int ring = P::ring_stages(p.ring_keys);

@@ -1,5 +1,6 @@
 // Parameter blocks and launchers shared by the host runtime (fb_runtime.cpp)
-// and the gfx950 kernels (fb_kernels.hip).  Not part of the public ABI.
+// and the gfx950 kernels (fb_attn_bf16.hip, fb_attn_f32.hip, fb_aux.hip).  Not
+// part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -170,7 +171,8 @@ struct ResetParams {
 
 enum AttnMode { kModePartial = 0, kModeMerge = 1 };
 
-// Launchers (fb_kernels.hip).  Return the launch status.
+// Launchers (fb_aux.hip; launch_attn dispatches to the attention kernel files).
+// Return the launch status.
 hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, hipStream_t s);
 hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s);
 hipError_t launch_decide(const DecideParams& p, hipStream_t s);

@@ -55,6 +55,10 @@ class Workload:
     gamma: float = 0.0
     seed: int = 0
     description: str = ""
+    # Explicit M per step instead of the update distribution (tests of the
+    # threshold's edges): m_seq[s] for step s >= 1, an int for every sequence
+    # or a tuple with one count per sequence; the positions are still drawn.
+    m_seq: tuple = ()
 
     @property
     def group(self) -> int:
@@ -187,7 +191,10 @@ def generate(w: Workload, seed: Optional[int] = None, prefix: Optional[int] = No
                 m = np.zeros(B, dtype=np.int32)
                 if s > 0:
                     for b in range(B):
-                        if w.update == "uniform":
+                        if w.m_seq:
+                            e = w.m_seq[s]
+                            m[b] = e[b] if isinstance(e, tuple) else e
+                        elif w.update == "uniform":
                             m[b] = rng.integers(0, int(w.update_a) + 1)
                         else:
                             m[b] = rng.binomial(int(w.update_a), w.update_b)

@@ -140,17 +140,6 @@ def run_oracle(inp: wl.Inputs, policy: Optional[str] = None) -> List[oracle.Bloc
                              tau=w.tau, gamma=w.gamma)
 
 
-def run_oracle_head(inp: wl.Inputs, b: int, h: int, policy: Optional[str] = None) -> oracle.BlockResult:
-    """The oracle for one (sequence, query head) of the first block, on that
-    head's own slices (heads are independent)."""
-    w = inp.workload
-    g = h // w.group
-    steps = oracle_steps(inp.blocks[0], slice(b, b + 1), slice(h, h + 1), slice(g, g + 1))
-    kp = wl.to_f64(inp.k_prefix[b:b + 1, g:g + 1])
-    vp = wl.to_f64(inp.v_prefix[b:b + 1, g:g + 1])
-    return oracle.run_block(kp, vp, kp.shape[2], steps, policy or w.policy, tau=w.tau, gamma=w.gamma)
-
-
 def compare_block(gpu: GpuBlock, ref: oracle.BlockResult, dtype: str, pairs=None, what="") -> dict:
     """Decisions bit-exact; outputs and cached A_out/L_out within tolerance.
 

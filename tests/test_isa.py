@@ -7,6 +7,8 @@ with the library's own flags), checked without a GPU.
   address, five where its SGPR base may have been written by a vector
   instruction just before.  A missing wait reads a stale register: the load
   goes to a wrong address.
+- The LDS address of every DMA load (M0) is written in the same basic block,
+  by a scalar instruction, or by a vector one far enough back.
 - No packed-fp32 vector instruction (v_pk_add/mul/fma_f32) appears: the
   build turns the feature off and no code writes them by hand.
 - The attention kernels use no scratch memory (nothing spills).
@@ -48,6 +50,46 @@ def test_dma_loads_carry_their_wait_states(attn_asm):
         uniform_base = re.search(r",\s*s\[\d+:\d+\]", ins[i]) is not None
         need = "s_nop 4" if uniform_base else "s_nop 0"
         assert ins[i - 1] == need, f"{ins[i]!r} preceded by {ins[i - 1]!r}, needs {need}"
+
+
+def _wait_states_between(lines, j, i):
+    """Wait states the instructions strictly between lines j and i provide:
+    s_nop N gives N + 1, any other instruction one."""
+    n = 0
+    for t in lines[j + 1:i]:
+        if not t or t.startswith((";", ".", "#")):
+            continue
+        m = re.match(r"s_nop\s+(\d+)", t)
+        n += int(m.group(1)) + 1 if m else 1
+    return n
+
+
+def test_dma_lds_address_is_set_by_a_scalar_write(attn_asm):
+    """M0 holds a DMA load's LDS address.  Its last writer before every load
+    sits in the same basic block, and is a scalar instruction (which needs one
+    wait state, supplied by the asm) or else a vector one at least five wait
+    states back (v_readfirstlane into M0: the compiler does not see the asm's
+    use of M0, so nothing else would space them)."""
+    lines = attn_asm
+    checked = 0
+    for i, l in enumerate(lines):
+        if not l.startswith("global_load_lds_dwordx4"):
+            continue
+        j = i - 1
+        while j >= 0:
+            t = lines[j]
+            assert not (t.endswith(":") and not t.startswith(";")), \
+                f"line {i}: M0 is set in another basic block than the DMA load"
+            if re.match(r"^[a-z_0-9]+\s+m0\b", t):
+                break
+            j -= 1
+        assert j >= 0, f"line {i}: no write of M0 before the DMA load"
+        writer = lines[j].split()[0]
+        need = 1 if writer.startswith("s_") else 5
+        got = _wait_states_between(lines, j, i)
+        assert got >= need, f"line {i}: {lines[j]!r} then {got} wait states before {l!r}, needs {need}"
+        checked += 1
+    assert checked > 100
 
 
 def test_no_packed_fp32_instructions(attn_asm, tmp_path):

@@ -2,9 +2,9 @@
 
 Decisions [step, batch, head] must be bit-exact; outputs, cached A_out and
 L_out within the tolerances.  Small variants (same distributions, shorter
-prefix) are compared on every head; the full-size workloads, run in the launch
-configuration the benchmark uses, are compared on sampled heads (heads are
-independent, so the oracle can evaluate one head alone).
+prefix) and the full-size workloads, run in the launch configuration the
+benchmark uses, are compared on every head.  The threshold's integer edges
+(M = tau recomputes, M = tau - 1 reuses) are driven with explicit counts.
 """
 import json
 import os
@@ -87,52 +87,71 @@ def test_dllm_full_size():
     _full_check(wl.workload("dllm-8k"))
 
 
-def _sampled(w, heads):
-    inp = wl.generate(w)
-    print(f"[parity] {w.name} full size, sampled heads {heads}", flush=True)
-    gpu = H.run_gpu(inp)[0]
-    for (b, h) in heads:
-        ref = H.run_oracle_head(inp, b, h)
-        errs = H.compare_block(gpu, ref, w.dtype, pairs=[((b, h), (0, 0))], what=f"{w.name} head ({b},{h})")
-        print(f"[parity] {w.name} head ({b},{h}) errs {errs}", flush=True)
-    return gpu, inp
-
-
-def test_long_full_size_sampled():
+def test_long_full_size():
+    """Batch 4 at the full 32768-token prefix, every head."""
     w = wl.workload("long-32k-b4")
-    gpu, inp = _sampled(w, [(0, 0), (1, 13), (2, 31), (3, 6)])
-    # tau decisions depend only on M: check every head against the rule
-    for s, m in enumerate(st.n_updated for st in inp.blocks[0].steps):
+    gpu, ref = _full_check(w)
+    # tau decisions depend only on M: every head follows its sequence's count
+    for s in range(ref[0].reuse.shape[0]):
         for b in range(w.batch):
-            expect = 0 if s == 0 else int(m[b] < w.tau)
-            assert np.all(gpu.reuse[s, b] == expect)
+            assert len(set(ref[0].reuse[s, b].tolist())) == 1
 
 
-def test_max_full_size_sampled():
-    _sampled(wl.workload("max-128k"), [(0, 0), (0, 21)])
+def test_max_full_size():
+    """The 131072-token prefix, block 64, every head."""
+    _full_check(wl.workload("max-128k"))
 
 
 def test_video_full_size():
-    """Full video workload: every decision against the stored float64 run,
-    outputs on sampled heads."""
+    """Full video workload, every head against the oracle; the decisions and
+    similarities also against the stored float64 run of the seed rule."""
     w = wl.workload("video-1560x15600")
     with open(os.path.join(GOLDEN, "video_seed.json")) as f:
         rec = json.load(f)
     assert rec["seed"] == w.seed
-    gpu, _ = _sampled(w, [(0, 1), (0, 4)])
-    np.testing.assert_array_equal(gpu.reuse, np.array(rec["reuse"], dtype=np.uint8))
+    gpu, ref = _full_check(w)
+    np.testing.assert_array_equal(gpu[0].reuse, np.array(rec["reuse"], dtype=np.uint8))
     ref_sim = np.array([[[np.nan if x is None else x for x in row] for row in st] for st in rec["sim"]])
     fin = ~np.isnan(ref_sim)
-    assert np.max(np.abs(gpu.sim[fin] - ref_sim[fin])) <= 5e-4
+    assert np.max(np.abs(gpu[0].sim[fin] - ref_sim[fin])) <= 5e-4
+    fin = ~np.isnan(ref[0].sim)
+    assert np.max(np.abs(gpu[0].sim[fin] - ref[0].sim[fin])) <= 5e-4
+
+
+@pytest.mark.parametrize("policy", ["tau", "tau_cum"])
+@pytest.mark.parametrize("device_counts", [False, True])
+def test_threshold_integer_edges(policy, device_counts):
+    """Explicit counts around tau = 8 on two sequences: M = tau recomputes and
+    M = tau - 1 reuses (strict <), in consecutive steps and in both orders;
+    under the cumulative rule the sums cross tau at known steps."""
+    tau = 8
+    m_seq = (0, (tau, tau - 1), (tau - 1, tau), (tau - 1, 0), (tau, 0), (0, tau - 1), (tau + 1, 1), (tau - 1, tau))
+    w = wl.workload("long-32k-b4").with_(batch=2, steps=len(m_seq), tau=tau, m_seq=m_seq, policy=policy)
+    inp = wl.generate(w, prefix=700)
+    print(f"[parity] threshold edges {policy} device_counts={device_counts}", flush=True)
+    gpu = H.run_gpu(inp, device_counts=device_counts)
+    ref = H.run_oracle(inp)
+    H.compare_block(gpu[0], ref[0], w.dtype, what=f"threshold edges {policy}")
+    per_seq = ref[0].reuse[:, :, 0].T.tolist()
+    if policy == "tau":
+        assert per_seq == [[0, 0, 1, 1, 0, 1, 0, 1], [0, 1, 0, 1, 1, 1, 1, 0]]
+    else:   # sum since the last computation, this step's included, against tau
+        # sequence 0: 8 | 7, 14 | 8 | 0, 9 | 7;  sequence 1: 7, 15 | 0, 0, 7, 8 | 8
+        assert per_seq == [[0, 0, 1, 0, 0, 1, 0, 1], [0, 1, 0, 1, 1, 1, 0, 0]], per_seq
 
 
 def test_deterministic():
-    """Repeated runs are bitwise identical (fixed-order reductions)."""
+    """Twenty repeated runs are bitwise identical (fixed-order reductions, no
+    float atomics): outputs, cached A_out and L_out."""
     w = wl.workload("dllm-8k").with_(steps=3)
     inp = wl.generate(w, prefix=2500)
-    runs = [H.run_gpu(inp, record_cache=False)[0].out for _ in range(3)]
-    for r in runs[1:]:
-        assert np.array_equal(r, runs[0])
+    first = H.run_gpu(inp)[0]
+    for _ in range(19):
+        r = H.run_gpu(inp)[0]
+        assert np.array_equal(r.out, first.out)
+        assert np.array_equal(r.a_out, first.a_out)
+        assert np.array_equal(r.l_out, first.l_out)
+        assert np.array_equal(r.reuse, first.reuse)
 
 
 def test_gamma_gqa_device_plan():
