@@ -10,18 +10,23 @@ prefix.  The stack holds enough layers that their prefix K/V exceed the
 256 MB MALL, as the layers of a model do, so every step streams its K/V from
 HBM without a cache flush in the timed region.
 
-Printed: one JSON line for the headline workload (the dLLM layer, batch 1,
-32/8 heads, prefix 8192, block 32).  ``value`` is the effective KV bandwidth:
-the prefix K/V bytes a recompute-every-step (ALWAYS) run would read, divided by
-the time taken under the workload's reuse policy.  ``roofline`` reports the
-recompute step's attention launch (block-external split-KV items plus the
-block-internal items it carries): algorithmic bytes per launch over its
-average launch duration (HIP events around each launch on its stream, in a profiled
-pass of the same steps under ALWAYS).  ``cpu_baseline`` times the float64
-oracle on the host cores.  ``workloads`` holds the same step and kernel
-figures, from fewer steps, for the other workloads.
+Printed: one JSON line for the headline workload, the largest single-GPU
+one (max-128k: batch 1, 32/8 heads, D=128, prefix 131072, block 64).
+``value`` is the effective KV bandwidth: the prefix K/V bytes a
+recompute-every-step (ALWAYS) run would read, divided by the time taken under
+the workload's reuse policy (it counts the bytes a reuse step does not read,
+so it can exceed the HBM peak).  ``roofline`` reports the recompute step's
+attention launch (block-external split-KV items plus the block-internal items
+it carries): algorithmic bytes per launch over its average launch duration
+(HIP events around each launch on its stream, in a profiled pass of the same
+steps under ALWAYS); its ``frac`` is the share of the HBM (or MFMA) roofline.
+``step_us`` gives median, p10 and p90 of at least 50 timed steps per kind.
+``cpu_baseline`` times the float64 oracle on the host cores.  ``workloads``
+holds the same step and kernel figures, from fewer steps, for the other
+workloads.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dllm-8k] [--no-extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload max-128k] [--no-extra]
+    python bench.py --always-only --workload NAME --steps K   (recompute steps only, for rocprofv3)
 """
 from __future__ import annotations
 
@@ -45,7 +50,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
-EXTRA = ["long-32k-b4", "max-128k", "video-1560x15600", "tiny-fp32"]
+EXTRA = ["long-32k-b4", "dllm-8k", "video-1560x15600", "tiny-fp32"]
+HEADLINE = "max-128k"
+PERCENTILE_REPS = 50
 
 
 def _code_text(src: str) -> str:
@@ -163,32 +170,49 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
     _, gpu_always = timed(fb.POLICY_ALWAYS)
 
     reuse_counts = []
-    step_full_us = step_reuse_us = None
+    step_stats = None
     if decisions:   # decisions of one block under the policy (the caches' own record)
         state["s"] = 0
         for _ in range(S):
             step(policy)
             reuse_counts.append(int(caches[0].read(fb.FIELD_REUSE).sum()))
         # per-step times (HIP events around each step of all layers), split into
-        # steps where some head recomputes ("full") and steps where all reuse
+        # steps where some head recomputes ("full") and steps where all reuse,
+        # whole blocks at a time until each kind has PERCENTILE_REPS samples
+        # (or the block has none of that kind); then always-recompute steps
         nh = w.batch * w.n_q_heads
-        state["s"] = 0
-        for _ in range(S):
-            step(policy)
-        state["s"] = 0
-        torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        evs[0].record()
-        for i in range(steps):
-            step(policy)
-            evs[i + 1].record()
-        torch.cuda.synchronize()
-        full, reuse = [], []
-        for i in range(steps):
-            us = 1e3 * evs[i].elapsed_time(evs[i + 1]) / layers
-            (reuse if reuse_counts[i % S] == nh else full).append(us)
-        step_full_us = float(np.median(full)) if full else None
-        step_reuse_us = float(np.median(reuse)) if reuse else None
+        n_full_blk = sum(1 for c in reuse_counts if c != nh)
+        n_reuse_blk = S - n_full_blk
+        need = max(math.ceil(PERCENTILE_REPS / max(1, n)) for n in
+                   ([n_full_blk] if n_full_blk else []) + ([n_reuse_blk] if n_reuse_blk else []))
+        reps = S * min(need, 64)
+
+        def per_step(pol, count):
+            state["s"] = 0
+            for _ in range(S):
+                step(pol)
+            state["s"] = 0
+            torch.cuda.synchronize()
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(count + 1)]
+            evs[0].record()
+            for i in range(count):
+                step(pol)
+                evs[i + 1].record()
+            torch.cuda.synchronize()
+            return [1e3 * evs[i].elapsed_time(evs[i + 1]) / layers for i in range(count)]
+
+        times = per_step(policy, reps)
+        full = [t for i, t in enumerate(times) if reuse_counts[i % S] != nh]
+        reuse = [t for i, t in enumerate(times) if reuse_counts[i % S] == nh]
+        always = per_step(fb.POLICY_ALWAYS, max(PERCENTILE_REPS, S))
+
+        def pct(xs):
+            if not xs:
+                return None
+            return {"median": round(float(np.median(xs)), 3), "p10": round(float(np.percentile(xs, 10)), 3),
+                    "p90": round(float(np.percentile(xs, 90)), 3), "n": len(xs)}
+
+        step_stats = {"full": pct(full), "all_reuse": pct(reuse), "always": pct(always)}
 
     # profiled pass under ALWAYS: every step launches the external kernel
     for c in caches:
@@ -222,8 +246,7 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
         "per_layer_step_us": 1e6 * gpu_s / steps / layers,
         "always_layer_step_us": 1e6 * gpu_always / steps / layers,
         "eff_gbs": kv_bytes * layers * steps / gpu_s / 1e9, "reuse_counts": reuse_counts,
-        "kernel_us": kernel_us, "roofline": roof, "policy": policy_name,
-        "step_full_us": step_full_us, "step_reuse_us": step_reuse_us,
+        "kernel_us": kernel_us, "roofline": roof, "policy": policy_name, "step_stats": step_stats,
     }
 
 
@@ -446,24 +469,32 @@ def staleness(name, policies):
                   "reused_fraction": round(float(reuse[pol].mean()), 4)} for pol in policies}
 
 
-def traffic_for(name):
-    """HBM bytes per external-attention launch from stored counters, while the
-    kernel sources are the ones they were taken on (else None)."""
+def counters_for(name):
+    """Stored counters of the recompute-step attention launch (HBM bytes per
+    launch, MFMA busy share), while the kernel sources are the ones they were
+    taken on (else None)."""
     pmc = os.path.join(ROOT, "profiles", f"pmc_{name}.json")
     if not os.path.exists(pmc):
         return None
     with open(pmc) as f:
         rec = json.load(f)
-    return rec.get("hbm_bytes_per_launch") if rec.get("kernel_source_hash") == kernel_source_hash() else None
+    return rec if rec.get("kernel_source_hash") == kernel_source_hash() else None
 
 
-def cpu_baseline(name, budget_s: float):
+def cpu_baseline(name, budget_s: float, threads=None):
     """The float64 oracle on the host cores, on the same workload's block:
     single-head runs in head order (starting over when every head is done)
-    until about budget_s seconds of work, scaled to all heads."""
-    import oracle
-    from threadpoolctl import threadpool_info
+    until about budget_s seconds of work, scaled to all heads.  threads: cap
+    the BLAS pool (None: every core it has)."""
+    import contextlib
+    from threadpoolctl import threadpool_info, threadpool_limits
     from cached_attention_fb_amd import workload as wl
+    with (threadpool_limits(threads) if threads else contextlib.nullcontext()):
+        return _cpu_baseline(name, budget_s, wl, threadpool_info)
+
+
+def _cpu_baseline(name, budget_s, wl, threadpool_info):
+    import oracle
 
     w = wl.workload(name)
     inp = wl.generate(w)
@@ -585,6 +616,56 @@ def sweep(prefixes=SWEEP_PREFIXES, n_blocks=3):
             "rows": rows}
 
 
+def always_only(name, steps, warmup):
+    """Recompute-every-step passes of a workload (every head recomputes at
+    every step), for profiler runs whose kernel averages must cover full
+    recompute launches only: `warmup` untimed steps, then `steps` timed ones
+    over the same layer stack as the benchmark."""
+    import torch
+    from cached_attention_fb_amd import fb
+    from cached_attention_fb_amd import workload as wl
+
+    w = wl.workload(name)
+    inp = wl.generate(w)
+    blk = inp.blocks[0]
+    S = len(blk.steps)
+    n = w.prefix
+    kv_bytes, _, _ = algorithmic(w, n)
+    layers = max(1, math.ceil(2.5 * MALL_BYTES / kv_bytes))
+    kp0, vp0 = inp.k_prefix.cuda(), inp.v_prefix.cuda()
+    prefixes = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(layers - 1)]
+    caches = [fb.Cache(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block, n, w.torch_dtype)
+              for _ in range(layers)]
+    qs = [st.q.cuda() for st in blk.steps]
+    ks = [st.k.cuda() for st in blk.steps]
+    vs = [st.v.cuda() for st in blk.steps]
+    del inp, blk
+    outs = [torch.empty_like(qs[0]) for _ in range(layers)]
+    prepared = [[c.prepare(qs[s], ks[s], vs[s], prefixes[li][0], prefixes[li][1], outs[li]) for s in range(S)]
+                for li, c in enumerate(caches)]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run(count):
+        for i in range(count):
+            s = i % S
+            for li, c in enumerate(caches):
+                if s == 0:
+                    c.reset(stream)
+                prepared[li][s](fb.POLICY_ALWAYS, n, None, 0, 0.0, stream)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / (steps * layers)
+    for c in caches:
+        c.close()
+    return {"always_only": name, "layers": layers, "steps": steps, "us_per_layer_step": round(us, 3)}
+
+
 def calibrate():
     """A plain elementwise kernel of known traffic (reads 256 MiB, writes
     256 MiB), run under the same counters as the attention kernels to scale
@@ -603,7 +684,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="dllm-8k")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--policy", default=None, choices=[None, "tau", "gamma", "always", "tau_cum", "gamma_group"])
     ap.add_argument("--layers", type=int, default=0, help="0: enough layers to exceed 2.5x the MALL")
     ap.add_argument("--splits", type=int, default=0, help="0: automatic split-KV count")
@@ -616,6 +697,8 @@ def main():
                     help="only run FlashBlock over a sparse attention at densities 0.2/0.3/0.4")
     ap.add_argument("--graph", action="store_true",
                     help="only run device-side threshold decisions, eager and as HIP graphs")
+    ap.add_argument("--always-only", action="store_true",
+                    help="only time recompute-every-step passes of --workload (profiling runs)")
     args = ap.parse_args()
     if args.calibrate:
         calibrate()
@@ -637,6 +720,9 @@ def main():
     if args.sparse:
         print(json.dumps(sparse_bench(args.workload)), flush=True)
         return
+    if args.always_only:
+        print(json.dumps(always_only(args.workload, args.steps, args.warmup)), flush=True)
+        return
 
     # the largest prefix one layer's K/V can take in the free device memory
     from cached_attention_fb_amd import workload as wl
@@ -645,7 +731,10 @@ def main():
     r = measure(args.workload, args.steps, args.warmup, args.policy, args.layers, args.splits)
     w = r["w"]
     roof = dict(r["roofline"])
-    roof["traffic"] = traffic_for(w.name)
+    ctr = counters_for(w.name)
+    roof["traffic"] = None if ctr is None else ctr.get("hbm_bytes_per_launch")
+    if ctr is not None and ctr.get("mfma_busy_frac") is not None:
+        roof["mfma_busy_frac"] = ctr["mfma_busy_frac"]   # SQ_VALU_MFMA_BUSY_CYCLES share, stored counters
     result = {
         "metric": METRIC,
         "value": round(r["eff_gbs"], 1),
@@ -666,8 +755,7 @@ def main():
         "always_us_per_layer_step": round(r["always_layer_step_us"], 3),
         "reuse_vs_full_speedup": round(r["always_layer_step_us"] / r["per_layer_step_us"], 3),
         "reused_heads_per_step": r["reuse_counts"],
-        "step_us_median": {"full": None if r["step_full_us"] is None else round(r["step_full_us"], 3),
-                           "all_reuse": None if r["step_reuse_us"] is None else round(r["step_reuse_us"], 3)},
+        "step_us": r["step_stats"],
         "ext_plus_combine_us": round(r["kernel_us"].get("external", 0.0) + r["kernel_us"].get("combine", 0.0), 3),
         "capacity_prefix_tokens_per_layer": capacity,
         "wall_s": round(r["wall_s"], 4),
@@ -682,13 +770,16 @@ def main():
             S = wl.workload(name).steps
             e = measure(name, 2 * S, S, decisions=False)
             rf = e["roofline"]
+            rc = counters_for(name)
             extra[name] = {"policy": e["policy"], "layers": e["layers"], "steps": 2 * S,
                            "us_per_layer_step": round(e["per_layer_step_us"], 2),
                            "always_us_per_layer_step": round(e["always_layer_step_us"], 2),
                            "reuse_vs_full_speedup": round(e["always_layer_step_us"] / e["per_layer_step_us"], 3),
                            "effective_kv_gbs": round(e["eff_gbs"], 1),
-                           "external": {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac",
-                                                           "avg_launch_us")},
+                           "external": {**{k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                                              "avg_launch_us")},
+                                        "traffic": None if rc is None else rc.get("hbm_bytes_per_launch"),
+                                        "mfma_busy_frac": None if rc is None else rc.get("mfma_busy_frac")},
                            "kernel_avg_us_always": e["kernel_us"]}
         result["workloads"] = extra
         # threshold variants (per-step vs cumulative M): step time, reuse and
@@ -705,11 +796,13 @@ def main():
                                        **err[pol]}
         result["policy_variants"] = variants
         # threshold decisions on the device, eager and replayed as HIP graphs
-        result["device_decisions"] = graph_bench(w.name if w.policy in ("tau", "tau_cum") else "dllm-8k")
+        result["device_decisions"] = graph_bench("dllm-8k")
         # FlashBlock over a sparse attention (left-out tiles cached, kept tiles fresh)
         result["sparse"] = {nm: sparse_bench(nm) for nm in ("dllm-8k", "long-32k-b4")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
+        if not args.no_extra:   # the small workloads' oracle on one thread
+            result["cpu_oracle_1thread"] = {nm: cpu_baseline(nm, 4.0, threads=1) for nm in ("tiny-fp32", "dllm-8k")}
     print(json.dumps(result), flush=True)
 
 
