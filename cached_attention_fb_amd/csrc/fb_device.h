@@ -392,8 +392,10 @@ __device__ __forceinline__ void merge_store(const AttnParams& p, const f32x16 (&
   }
 }
 
-// Launchers of the two attention kernel families.
+// Launchers of the attention kernel families: fp32, bf16 (32 rows per wave),
+// and bf16 with 64 rows per wave (partial launches of 256-row groups, D=128).
 hipError_t launch_attn_f32(int head_dim, int mode, const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_bf16(int head_dim, int mode, const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_r64(const AttnParams& p, hipStream_t s);
 
 }  // namespace fbk

@@ -58,6 +58,29 @@ struct ProfRec {
   hipEvent_t start, stop;
 };
 
+// Split counts chosen so far, keyed by (keys, active groups, co-scheduled
+// workgroups, their tiles); a fixed table (no allocation), the oldest entry
+// replaced when full.
+struct SplitMemo {
+  static constexpr int kCap = 256;
+  struct Entry {
+    int32_t keys, groups, co_items, co_tiles, splits;
+  } e[kCap];
+  int n = 0, next = 0;
+  int find(int keys, int groups, int co_items, int co_tiles) const {
+    for (int i = 0; i < n; ++i)
+      if (e[i].keys == keys && e[i].groups == groups && e[i].co_items == co_items && e[i].co_tiles == co_tiles)
+        return e[i].splits;
+    return -1;
+  }
+  void put(int keys, int groups, int co_items, int co_tiles, int splits) {
+    e[next] = Entry{keys, groups, co_items, co_tiles, splits};
+    next = (next + 1) % kCap;
+    n = n < kCap ? n + 1 : kCap;
+  }
+  void clear() { n = next = 0; }
+};
+
 }  // namespace
 
 struct fb_cache {
@@ -80,8 +103,7 @@ struct fb_cache {
   int dyn_grid = 0;      // workgroups of the largest item count over the plan
   int dyn_kps = 0;       // longest key range of the plan
   int dyn_co = 0;        // co-scheduled workgroups the plan was made for
-  // split counts chosen so far: (keys, active groups, co workgroups, their tiles)
-  std::map<std::tuple<int, int, int, int>, int> split_memo;
+  SplitMemo split_memo;   // split counts chosen so far
   int n_cu = 256;        // compute units of the device
   float scale = 0.0f;
   size_t bytes = 0;
@@ -143,26 +165,54 @@ fb_status check_config(const fb_config* cfg) {
 
 // Time in tiles of a launch whose first co_items workgroups take co_tiles
 // tiles each and whose ext_wgs others take `per`: every CU runs one workgroup
-// at a time and takes the next one (in launch order) as it frees up.
+// at a time and takes the next one (in launch order) as it frees up.  The
+// moments at which CUs free up are kept as (time, CUs) pairs in a fixed,
+// time-ordered table (no allocation; a launch has few distinct moments).
 long span_with_co_items(int n_cu, long co_items, long co_tiles, long ext_wgs, long per) {
-  std::map<long, long> free_at;   // time -> CUs that free up then
-  free_at[0] = n_cu;
+  constexpr int kCap = 512;
+  long t_at[kCap], n_at[kCap];
+  int len = 1;
+  t_at[0] = 0;
+  n_at[0] = n_cu;
+  auto add = [&](long t, long n) {   // insert keeping times ascending, merging equal times
+    int i = 0;
+    while (i < len && t_at[i] < t) ++i;
+    if (i < len && t_at[i] == t) {
+      n_at[i] += n;
+      return;
+    }
+    if (len == kCap) {   // out of room: fold into the last moment (a longer span, never a shorter one)
+      n_at[len - 1] += n;
+      t_at[len - 1] = std::max(t_at[len - 1], t);
+      return;
+    }
+    for (int j = len; j > i; --j) {
+      t_at[j] = t_at[j - 1];
+      n_at[j] = n_at[j - 1];
+    }
+    t_at[i] = t;
+    n_at[i] = n;
+    ++len;
+  };
   long qi = co_items, qe = ext_wgs, end = 0;
-  while (qi + qe > 0 && !free_at.empty()) {
-    const auto it = free_at.begin();
-    const long t = it->first;
-    long n = it->second;
-    free_at.erase(it);
+  while (qi + qe > 0 && len > 0) {
+    const long t = t_at[0];
+    long n = n_at[0];
+    for (int j = 1; j < len; ++j) {   // pop the earliest moment
+      t_at[j - 1] = t_at[j];
+      n_at[j - 1] = n_at[j];
+    }
+    --len;
     const long a = std::min(n, qi);
     if (a > 0) {
-      free_at[t + co_tiles] += a;
+      add(t + co_tiles, a);
       qi -= a;
       n -= a;
       end = std::max(end, t + co_tiles);
     }
     const long b = std::min(n, qe);
     if (b > 0) {
-      free_at[t + per] += b;
+      add(t + per, b);
       qe -= b;
       end = std::max(end, t + per);
     }
@@ -184,9 +234,8 @@ int choose_splits(fb_cache* c, int n_keys, int active_groups, int co_items = 0, 
   if (c->kv_splits > 0) {
     want = c->kv_splits;
   } else {
-    const auto key = std::make_tuple(n_keys, active_groups, co_items, co_tiles);
-    const auto hit = c->split_memo.find(key);
-    if (hit != c->split_memo.end()) return hit->second;
+    const int hit = c->split_memo.find(n_keys, active_groups, co_items, co_tiles);
+    if (hit >= 0) return hit;
     const int base = std::max(1, active_groups * c->row_tiles);
     const int smax = std::max(1, std::min({tiles / 2, c->splits_cap, fbk::kMaxSplits}));
     // makespan in tiles: rounds of workgroups x tiles per chunk, after
@@ -203,8 +252,7 @@ int choose_splits(fb_cache* c, int n_keys, int active_groups, int co_items = 0, 
     want = std::max(1, std::min({want, tiles, c->splits_cap}));
     const int tiles_per = (tiles + want - 1) / want;
     const int sp = (tiles + tiles_per - 1) / tiles_per;   // no empty chunk
-    if (c->split_memo.size() >= 4096) c->split_memo.clear();   // bounded: prefixes grow block by block
-    c->split_memo[key] = sp;
+    c->split_memo.put(n_keys, active_groups, co_items, co_tiles, sp);
     return sp;
   }
   want = std::max(1, std::min({want, tiles, c->splits_cap}));
