@@ -33,6 +33,7 @@ SOURCES = {
     "fb_attn_r64.hip": VGPR_FORM,
     "fb_attn_f32.hip": VGPR_FORM,
     "fb_aux.hip": VGPR_FORM,
+    "fb_noalloc.hip": [],
     "fb_runtime.cpp": [],
 }
 

@@ -180,6 +180,14 @@ hipError_t launch_reset(const ResetParams& p, hipStream_t s);
 hipError_t launch_complement(const ComplementParams& p, hipStream_t s);
 hipError_t launch_record(const HeadSel& sel, uint8_t* rec, int n_heads, int hq, hipStream_t s);
 
+// Sets the calling thread's error message (fb_last_error) and returns code.
+fb_status report(fb_status code, const char* msg);
+
+// fb_step_noalloc's work on a given scratch buffer (fb_runtime.cpp).
+fb_status noalloc_step(const fb_config* cfg, void* scratch, size_t scratch_bytes, int n_cu, const void* q_blk,
+                       const void* k_blk, const void* v_blk, const void* k_prefix, const void* v_prefix,
+                       int32_t prefix_len, float* a_out, float* l_out, void* out, void* stream);
+
 // ceil(2^32 / d): then n / d = floor(n * m / 2^32) exactly for every n with
 // n * d < 2^32 (the rounding up of m adds less than n / 2^32 < 1 / d).  0
 // (an ordinary division) when some index below n_max breaks that bound.

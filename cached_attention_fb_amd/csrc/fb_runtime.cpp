@@ -120,6 +120,8 @@ struct fb_cache {
   float* tot_o = nullptr;    // [B][Hq][Bs][D] sparse steps: cached part merged with the kept keys' part
   float* tot_l = nullptr;    // [B][Hq][Bs]
   int32_t* comp = nullptr;   // [B*Hkv][comp_stride] sparse steps: prefix tiles the selection leaves out
+  int64_t part_o_stride_override = 0;   // > 0: distance of the partials' slots in elements (caller scratch)
+  int64_t part_l_stride_override = 0;
   int comp_stride = 1;       // ceil(max_prefix / 64), at least 1
   // host state
   int64_t steps = 0;         // fb_step calls since the last reset
@@ -427,8 +429,8 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   p.reuse_rec = o.rec;
   p.part_o = c->part_o;
   p.part_l = c->part_l;
-  p.part_o_stride = elems_per_slot(c->cfg);
-  p.part_l_stride = rows_per_slot(c->cfg);
+  p.part_o_stride = c->part_o_stride_override > 0 ? c->part_o_stride_override : elems_per_slot(c->cfg);
+  p.part_l_stride = c->part_l_stride_override > 0 ? c->part_l_stride_override : rows_per_slot(c->cfg);
   ProfRec r;
   hipError_t e = hipSuccess;
   if (p.grid > 0) {
@@ -553,6 +555,31 @@ const char* fb_last_error(void) { return g_err.c_str(); }
 
 namespace {
 
+// Launch shapes of a cache of this config (no device state).
+void setup_shape(fb_cache* c, const fb_config* cfg) {
+  c->cfg = *cfg;
+  c->group = cfg->n_q_heads / cfg->n_kv_heads;
+  c->rows = c->group * cfg->block_size;
+  if (cfg->dtype == FB_BF16) {
+    // up to 128 rows: 4 row waves + 4 waves on the other key half of each
+    // tile; more rows: 8 row waves; 32 rows or fewer: a single wave
+    if (c->rows <= 32) c->ext_waves = 1, c->ext_ksplit = 1;
+    else if (c->rows <= 128) c->ext_waves = 8, c->ext_ksplit = 2;
+    else c->ext_waves = 8, c->ext_ksplit = 1;
+    // block-internal attention: one wave per 32 rows for small blocks, the
+    // split-key 8-wave shape for frame-sized ones
+    if (c->rows >= 512) c->int_waves = 8, c->int_ksplit = 2;
+    else c->int_waves = 1, c->int_ksplit = 1;
+  } else {
+    c->ext_waves = c->int_waves = 4;   // the fp32 kernel has a fixed shape
+  }
+  const int ext_rows_per_wg = 32 * c->ext_waves / c->ext_ksplit;
+  c->row_tiles = (c->rows + ext_rows_per_wg - 1) / ext_rows_per_wg;
+  const int crows = fbk::combine_rows(cfg->head_dim);
+  c->row_chunks = (cfg->block_size + crows - 1) / crows;
+  c->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
+}
+
 // Copies a caller's options struct that starts with its own size: the bytes
 // the caller has (at most sizeof(T)); fields past them keep T's defaults.
 template <typename T>
@@ -579,29 +606,9 @@ fb_status alloc_impl(const fb_config* cfg, int kv_splits, fb_cache** out) {
 
   fb_cache* c = new (std::nothrow) fb_cache();
   if (!c) return fail(FB_E_NOMEM, "host allocation failed");
-  c->cfg = *cfg;
+  setup_shape(c, cfg);
   c->kv_splits = kv_splits;
   c->device = dev;
-  c->group = cfg->n_q_heads / cfg->n_kv_heads;
-  c->rows = c->group * cfg->block_size;
-  if (cfg->dtype == FB_BF16) {
-    // up to 128 rows: 4 row waves + 4 waves on the other key half of each
-    // tile; more rows: 8 row waves; 32 rows or fewer: a single wave
-    if (c->rows <= 32) c->ext_waves = 1, c->ext_ksplit = 1;
-    else if (c->rows <= 128) c->ext_waves = 8, c->ext_ksplit = 2;
-    else c->ext_waves = 8, c->ext_ksplit = 1;
-    // block-internal attention: one wave per 32 rows for small blocks, the
-    // split-key 8-wave shape for frame-sized ones
-    if (c->rows >= 512) c->int_waves = 8, c->int_ksplit = 2;
-    else c->int_waves = 1, c->int_ksplit = 1;
-  } else {
-    c->ext_waves = c->int_waves = 4;   // the fp32 kernel has a fixed shape
-  }
-  const int ext_rows_per_wg = 32 * c->ext_waves / c->ext_ksplit;
-  c->row_tiles = (c->rows + ext_rows_per_wg - 1) / ext_rows_per_wg;
-  const int crows = fbk::combine_rows(cfg->head_dim);
-  c->row_chunks = (cfg->block_size + crows - 1) / crows;
-  c->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
   c->host_valid.assign(cfg->batch, 0);
   c->cum_updated.assign(cfg->batch, 0);
   {
@@ -1025,3 +1032,62 @@ fb_status fb_profile_read(fb_cache* c, fb_profile_stats* out) {
 }
 
 }  // extern "C"
+
+namespace fbk {
+
+fb_status report(fb_status code, const char* msg) { return code == FB_OK ? ok() : fail(code, "%s", msg); }
+
+// One always-recompute step on caller buffers, with its split partials and
+// per-head flags in `scratch` (scratch_bytes): the path of fb_step under
+// FB_POLICY_ALWAYS, whose cached A_out/L_out are the caller's a_out/l_out.
+// The cache object lives on the stack and its tables are fixed arrays, so
+// nothing is allocated, on the host or the device.
+fb_status noalloc_step(const fb_config* cfg, void* scratch, size_t scratch_bytes, int n_cu, const void* q_blk,
+                       const void* k_blk, const void* v_blk, const void* k_prefix, const void* v_prefix,
+                       int32_t prefix_len, float* a_out, float* l_out, void* out, void* stream) {
+  fb_status st = check_config(cfg);
+  if (st != FB_OK) return st;
+  if (!q_blk || !k_blk || !v_blk || !a_out || !l_out || !out) return fail(FB_E_ARG, "a tensor pointer is null");
+  if (prefix_len < 0 || prefix_len > cfg->max_prefix)
+    return fail(FB_E_SHAPE, "prefix_len %d outside [0, max_prefix=%d]", prefix_len, cfg->max_prefix);
+  if (prefix_len > 0 && (!k_prefix || !v_prefix)) return fail(FB_E_ARG, "k_prefix/v_prefix is null");
+  fb_cache c;
+  setup_shape(&c, cfg);
+  if (n_cu > 0) c.n_cu = n_cu;
+  // scratch: valid and reuse flags [B*Hq] each, then the split partials, L
+  // (fp32) and A (the working dtype), for as many splits as fit (the last
+  // slot holds the block-internal part)
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t nh = (size_t)cfg->batch * cfg->n_q_heads;
+  const size_t part_a = (size_t)elems_per_slot(*cfg) * (cfg->dtype == FB_BF16 ? 2 : 4);
+  const size_t part_l = (size_t)rows_per_slot(*cfg) * sizeof(float);
+  const size_t fixed = 2 * up(nh);
+  const size_t per_slot = up(part_l) + up(part_a);
+  if (scratch_bytes < fixed + 2 * per_slot)
+    return fail(FB_E_SHAPE, "this shape needs %zu bytes of scratch with a single prefix chunk; the limit is %zu",
+                fixed + 2 * per_slot, scratch_bytes);
+  const int slots = (int)std::min<size_t>((scratch_bytes - fixed) / per_slot, fbk::kMaxSplits + 1);
+  c.splits_cap = slots - 1;
+  char* base = static_cast<char*>(scratch);
+  c.valid = reinterpret_cast<uint8_t*>(base);
+  c.reuse = reinterpret_cast<uint8_t*>(base + up(nh));
+  c.part_l = reinterpret_cast<float*>(base + fixed);
+  c.part_o = reinterpret_cast<float*>(base + fixed + (size_t)slots * up(part_l));
+  c.slot_o = a_out;
+  c.slot_l = l_out;
+  // part_l's slots are up(part_l) apart; the strides run in elements
+  c.part_l_stride_override = (int64_t)(up(part_l) / sizeof(float));
+  c.part_o_stride_override = (int64_t)(up(part_a) / (cfg->dtype == FB_BF16 ? 2 : 4));
+  fbk::HeadSel sel = all_heads(&c);
+  ExtOpts eo;
+  eo.kblk = k_blk;
+  eo.vblk = v_blk;
+  eo.out = out;
+  eo.rec = c.reuse;
+  eo.follow_rec = false;
+  st = run_external(&c, q_blk, k_prefix, v_prefix, dense_keys(prefix_len), sel, cfg->batch * cfg->n_kv_heads,
+                    (hipStream_t)stream, eo);
+  return st == FB_OK ? ok() : st;
+}
+
+}  // namespace fbk

@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "FB_OK", 1: "FB_E_ARG", 2: "FB_E_SHAPE", 3: "FB_E_DTYPE", 4: 
 
 EXPORTED = ["fb_cache_alloc", "fb_cache_alloc_ex", "fb_cache_free", "fb_cache_reset", "fb_external_attn",
             "fb_internal_attn_merge", "fb_step", "fb_step_ex", "fb_step_sparse", "fb_cache_read",
-            "fb_cache_info", "fb_profile_enable", "fb_profile_read", "fb_last_error"]
+            "fb_cache_info", "fb_profile_enable", "fb_profile_read", "fb_step_noalloc", "fb_last_error"]
 
 
 class FBConfig(ctypes.Structure):
@@ -92,6 +92,7 @@ def load() -> ctypes.CDLL:
     lib.fb_cache_info.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32)]
     lib.fb_profile_enable.argtypes = [vp, i32]
     lib.fb_profile_read.argtypes = [vp, ctypes.POINTER(FBProfileStats)]
+    lib.fb_step_noalloc.argtypes = [ctypes.POINTER(FBConfig), vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
     for name in EXPORTED[:-1]:
         getattr(lib, name).restype = st
     lib.fb_last_error.argtypes = []
@@ -267,6 +268,35 @@ class Cache:
             self.close()
         except Exception:
             pass
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def step_noalloc(q, k_blk, v_blk, k_prefix, v_prefix, prefix_len: int, a_out, l_out, out,
+                 softmax_scale: float = 0.0, stream=None) -> None:
+    """fb_step_noalloc: one always-recompute step with no cache and no
+    allocation.  Shapes: q, out [B, Hq, Bs, D]; k_blk, v_blk [B, Hkv, Bs, D];
+    k_prefix, v_prefix [B, Hkv, max_prefix, D] (working dtype); a_out float32
+    [B, Hq, Bs, D]; l_out float32 [B, Hq, Bs]; all contiguous device tensors."""
+    lib = load()
+    b, hq, bs, d = q.shape
+    hkv, max_prefix = k_prefix.shape[1], k_prefix.shape[2]
+    dt = FB_F32 if q.dtype == torch.float32 else FB_BF16 if q.dtype == torch.bfloat16 else -1
+    cfg = FBConfig(b, hq, hkv, d, bs, max_prefix, dt, softmax_scale)
+    for t, shape, name in ((q, (b, hq, bs, d), "q"), (out, (b, hq, bs, d), "out"), (k_blk, (b, hkv, bs, d), "k_blk"),
+                           (v_blk, (b, hkv, bs, d), "v_blk"), (v_prefix, tuple(k_prefix.shape), "v_prefix"),
+                           (a_out, (b, hq, bs, d), "a_out"), (l_out, (b, hq, bs), "l_out")):
+        if tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor of shape {shape}")
+    if a_out.dtype != torch.float32 or l_out.dtype != torch.float32:
+        raise TypeError("a_out and l_out are float32")
+    for t, name in ((k_blk, "k_blk"), (v_blk, "v_blk"), (k_prefix, "k_prefix"), (v_prefix, "v_prefix"), (out, "out")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    _check(lib.fb_step_noalloc(ctypes.byref(cfg), q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
+                               k_prefix.data_ptr(), v_prefix.data_ptr(), int(prefix_len), a_out.data_ptr(),
+                               l_out.data_ptr(), out.data_ptr(), _stream(stream)))
 
 
 class PreparedStep:

@@ -253,6 +253,28 @@ fb_status fb_step_sparse(fb_cache* c, const fb_policy_args* p, const fb_step_opt
                          const void* k_prefix, const void* v_prefix, int32_t prefix_len,
                          const int32_t* sel_tiles, int32_t n_sel, void* out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): one
+ * denoising step that recomputes every head, as fb_step under
+ * FB_POLICY_ALWAYS, without a cache.  Its split partials and per-head flags
+ * use a library-owned static device array of FB_NOALLOC_SCRATCH_BYTES per GPU
+ * (held until the process ends; its device address is looked up at the
+ * first call on each device); nothing is allocated.
+ *   cfg      as for fb_cache_alloc (max_prefix = the prefix buffers' rows)
+ *   a_out    device float [B][Hq][Bs][D]: block-external output A_out
+ *   l_out    device float [B][Hq][Bs]: its log-normaliser L_out
+ *   out      device [B][Hq][Bs][D] in cfg's dtype: the merged output
+ * Other tensors as for fb_step.  The prefix is cut into as many chunks as the
+ * scratch holds (at most as many as fb_step would use).  Calls that overlap
+ * on one GPU share its array and race.  Asynchronous on `stream`.
+ * Errors: those of fb_cache_alloc's config checks, FB_E_ARG (null),
+ * FB_E_SHAPE (prefix_len out of range, or a shape whose partials for a single
+ * chunk exceed the scratch), FB_E_HIP. */
+#define FB_NOALLOC_SCRATCH_BYTES (64u << 20)
+fb_status fb_step_noalloc(const fb_config* cfg, const void* q_blk, const void* k_blk, const void* v_blk,
+                          const void* k_prefix, const void* v_prefix, int32_t prefix_len, float* a_out,
+                          float* l_out, void* out, void* stream);
+
 /* Copy one field of the cache (layouts in the FB_FIELD_* list) to host
  * memory `host_dst` of exactly `bytes` bytes, after the work already on
  * `stream`.  Synchronising; meant for tests and debugging.

@@ -167,6 +167,7 @@ def test_null_arguments():
     assert lib.fb_step_sparse(None, ctypes.byref(pa), None, None, None, None, None, None, 0, None, 0, None,
                               None) == fb.FB_E_ARG
     assert lib.fb_cache_alloc_ex(None, None, None) == fb.FB_E_ARG
+    assert lib.fb_step_noalloc(None, None, None, None, None, None, 0, None, None, None, None) == fb.FB_E_ARG
     assert lib.fb_cache_read(None, 0, None, 0, None) == fb.FB_E_ARG
     assert lib.fb_cache_info(None, None, None) == fb.FB_E_ARG
     assert lib.fb_profile_enable(None, 1) == fb.FB_E_ARG
