@@ -23,6 +23,7 @@
 #include <atomic>
 #include <cstdlib>
 
+#include "fb_combine.h"
 #include "fb_device.h"
 #include "fb_lds.h"
 
@@ -33,7 +34,9 @@ namespace {
 // Epilogue of a partial through LDS: normalise, write this wave's 32 rows to
 // `st` (row-major, 16-byte chunk c of row r at c ^ (r % (D/4))), read them
 // back as whole rows and store D/4 lanes per row.  nrows = valid rows.
-template <int D>
+// COH (the single-launch step): the partials are stored as device-coherent
+// relaxed atomics (past the XCD's L2), for a combine in the same launch.
+template <int D, bool COH>
 __device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f32x16 (&o)[D / 32], float m,
                                                    float ltot, int split, int64_t grow0, int nrows,
                                                    FB_LDS float* st, int lane) {
@@ -54,14 +57,25 @@ __device__ __forceinline__ void store_partial_rows(const AttnParams& p, const f3
   }
   // streaming stores: the partials leave this launch for the combine, and
   // kept out of L2 they need no write-back when the launch ends
-  if (hl == 0 && rl < nrows) __builtin_nontemporal_store(lse, p.part_l + split * p.part_l_stride + grow0 + rl);
+  if (hl == 0 && rl < nrows) {
+    float* dl = p.part_l + split * p.part_l_stride + grow0 + rl;
+    if constexpr (COH) __hip_atomic_store(dl, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else __builtin_nontemporal_store(lse, dl);
+  }
   bf16* od = reinterpret_cast<bf16*>(p.part_o) + split * p.part_o_stride + grow0 * D;
 #pragma unroll
   for (int k = 0; k < 32 / kRowsPerOp; ++k) {
     const int r = k * kRowsPerOp + lane / kC, c = lane % kC;
     const f32x4 v = *reinterpret_cast<const FB_LDS f32x4*>(st + r * D + ((c ^ (r & (kC - 1))) * 4));
     const bf16x4 vb = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-    if (r < nrows) __builtin_nontemporal_store(vb, reinterpret_cast<bf16x4*>(od + (int64_t)r * D + 4 * c));
+    if (r < nrows) {
+      bf16x4* dst = reinterpret_cast<bf16x4*>(od + (int64_t)r * D + 4 * c);
+      if constexpr (COH)
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), __builtin_bit_cast(uint64_t, vb), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else
+        __builtin_nontemporal_store(vb, dst);
+    }
   }
 }
 
@@ -73,8 +87,10 @@ constexpr int xch_bytes() { return ROWW * (4 * (D / 32) + 1) * 64 * 16; }
 // AUX: cache policy of the K/V DMA loads (see issue_tile).  ONE: the launch
 // gives every item at most one key tile (short blocks), so the loop body runs
 // once at most and carries no refill.
-template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT, bool LIST, int AUX, bool ONE>
-__global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const AttnParams p) {
+// One work item of a workgroup (it.ok): the attention of its rows over its
+// key range, and its epilogue.
+template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT, bool LIST, int AUX, bool ONE, bool COH = false>
+__device__ __forceinline__ void attn_body(const AttnParams& p, const AttnItem& it) {
   constexpr int WAVES = ROWW * KSPLIT;
   constexpr int NH = 2 / KSPLIT;   // 32-key halves of a tile per wave
   using P = Pipe<D, WAVES>;
@@ -83,14 +99,9 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
   extern __shared__ char smem_raw[];
   FB_LDS char* lds = (FB_LDS char*)smem_raw;
 
-  prefetch_params(p);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rw = wave % ROWW, kh = wave / ROWW;
   const int rl = lane & 31, hl = lane >> 5;
-  // ONE: a 3-D grid (row tile, kv head, sequence), one key range per group
-  const AttnItem it = ONE ? grid_item(p) : attn_item(p, MODE == kModePartial);
-  if constexpr (MODE == kModePartial) record_decisions(p);
-  if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
   const int b = it.b, g = it.g, grp = p.grp;
   const int key_begin = it.key_begin, key_end = it.key_end;
   const int ntiles_all = key_end > key_begin ? (key_end - key_begin + kKeyTile - 1) / kKeyTile : 0;
@@ -439,7 +450,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     if (!wave_live) return;
     const float ltot = pair_sum(lsum);
     constexpr int kRegionFloats = KSPLIT == 2 ? (4 * kDt + 1) * 64 * 4 : 32 * D;
-    store_partial_rows<D>(p, o, m, ltot, it.split, grow - rl, min(32, p.rows - row0),
+    store_partial_rows<D, COH>(p, o, m, ltot, it.split, grow - rl, min(32, p.rows - row0),
                           (FB_LDS float*)lds + rw * kRegionFloats, lane);
     return;
   }
@@ -451,6 +462,79 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const Att
     // The decision record goes last: a store issued before the merge would
     // hold up its wait for the cached part's loads (one counter for both).
     if (p.reuse_rec != nullptr && hl == 0 && (row % p.bs) == 0) p.reuse_rec[bh] = head_selected(p.sel, b, bh) ? 0 : 1;
+  }
+}
+
+template <int D, int ROWW, int KSPLIT, int MODE, bool PREFETCH_EXT, bool LIST, int AUX, bool ONE>
+__global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_bf16_kernel(const AttnParams p) {
+  prefetch_params(p);
+  // ONE: a 3-D grid (row tile, kv head, sequence), one key range per group
+  const AttnItem it = ONE ? grid_item(p) : attn_item(p, MODE == kModePartial);
+  if constexpr (MODE == kModePartial) record_decisions(p);
+  if (!it.ok) return;   // workgroup-uniform: no selected head, or past the device plan's items
+  attn_body<D, ROWW, KSPLIT, MODE, PREFETCH_EXT, LIST, AUX, ONE>(p, it);
+}
+
+// Single-launch fused step (see FinParams).  A combine workgroup polls its
+// group's counter every s_sleep 16 (about 0.5 us) and gives up after
+// kFinSpin polls (about 0.3 s in all): it sets the error flag and folds what
+// it finds.  One lane per workgroup touches a counter, each counter on a
+// line of its own.
+constexpr int kFinSpin = 1 << 19;
+
+// An attention workgroup is done with its item: every wave waits until its
+// partial stores (device-coherent) have completed, then the workgroup counts
+// itself in its group.
+__device__ __forceinline__ void fin_arrive(const FinParams& f, int group) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(f.ctr + (kFinCounters + group) * kFinStride, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Combine item c = (query head, chunk): the workgroup waits for its group's
+// attention items, each wave folds its rows (the combine kernel's fold, rows
+// 256/D * (chunk * WAVES + wave) ..), and the workgroup counts itself out;
+// the group's last combine workgroup returns the counter to zero.
+template <int D, int WAVES, int BATCH>
+__device__ __forceinline__ void fin_combine(const FinParams& f, int c) {
+  const CombineParams& p = f.cp;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int bh = c / f.chunks, chunk = c - bh * f.chunks;
+  const int b = bh / p.hq, h = bh - b * p.hq;
+  uint32_t* cnt = f.ctr + (kFinCounters + b * p.hkv + h / (p.hq / p.hkv)) * kFinStride;
+  if (threadIdx.x == 0) {
+    for (int i = 0;; ++i) {
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= f.need) break;
+      if (i == kFinSpin) {
+        __hip_atomic_fetch_or(f.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(16);
+    }
+  }
+  __syncthreads();   // the partials are read (device-coherent loads) after the arrivals were seen
+  const int ch = chunk * WAVES + wave;
+  if (ch < p.row_chunks) combine_fold<D, BATCH, true, true>(p, ch, bh, b, lane);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t o = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (o + 1 == f.done_all) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int D, int ROWW, int KSPLIT, int AUX, int BATCH>
+__global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_fin_kernel(const AttnParams p, const FinParams f) {
+  prefetch_params(p);
+  prefetch_params(f);
+  if ((int)blockIdx.x < f.n_attn) {   // workgroup-uniform
+    const AttnItem it = attn_item(p, true, blockIdx.x, f.n_attn);
+    record_decisions(p);
+    if (it.ok) attn_body<D, ROWW, KSPLIT, kModePartial, false, false, AUX, false, true>(p, it);
+    fin_arrive(f, it.b * p.hkv + it.g);
+  } else {
+    fin_combine<D, ROWW * KSPLIT, BATCH>(f, blockIdx.x - f.n_attn);
   }
 }
 
@@ -485,6 +569,40 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   hipLaunchKernelGGL((attn_bf16_kernel<D, ROWW, KSPLIT, MODE, PF, LIST, AUX, ONE>), grid, dim3(64 * ROWW * KSPLIT),
                      lds, s, with_div_magic(p, blocks));
   return hipGetLastError();
+}
+
+template <int D, int ROWW, int KSPLIT, int BATCH>
+hipError_t launch_fin(const AttnParams& p, const FinParams& f, hipStream_t s) {
+  using P = Pipe<D, ROWW * KSPLIT>;
+  constexpr int kStageOut = ROWW * 32 * D * 4;
+  constexpr int kQBytes = ROWW * 32 * D * 2;
+  constexpr int kMaxLds = std::max({P::kLdsBytes, P::q_offset(P::kStages, ROWW) + kQBytes,
+                                    (P::kStages - 1) * P::kStageBytes + kQBytes,
+                                    KSPLIT == 2 ? xch_bytes<D, ROWW>() : 0, kStageOut});
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (bit == 0 || (attr_done.load(std::memory_order_acquire) & bit) == 0) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_fin_kernel<D, ROWW, KSPLIT, 2, BATCH>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_done.fetch_or(bit, std::memory_order_release);
+  }
+  const int ring = P::ring_stages(p.ring_keys);
+  int lds = std::max(ring * P::kStageBytes, P::q_offset(ring, ROWW) + kQBytes);
+  if (KSPLIT == 2) lds = std::max(lds, xch_bytes<D, ROWW>());
+  lds = std::max(lds, kStageOut);
+  hipLaunchKernelGGL((attn_fin_kernel<D, ROWW, KSPLIT, 2, BATCH>), dim3(f.n_total), dim3(64 * ROWW * KSPLIT), lds, s,
+                     with_div_magic(p, f.n_attn), f);
+  return hipGetLastError();
+}
+
+template <int D, int ROWW, int KSPLIT>
+hipError_t launch_fin_batch(const AttnParams& p, const FinParams& f, hipStream_t s) {
+  if (f.cp.splits <= 8) return launch_fin<D, ROWW, KSPLIT, 8>(p, f, s);
+  if (f.cp.splits <= 16) return launch_fin<D, ROWW, KSPLIT, 16>(p, f, s);
+  return launch_fin<D, ROWW, KSPLIT, 32>(p, f, s);
 }
 
 // Streaming K/V: in a partial launch with one row tile per group every K/V
@@ -537,6 +655,20 @@ hipError_t launch_attn_bf16(int head_dim, int mode, const AttnParams& p, hipStre
   if (head_dim == 64)
     return mode == kModePartial ? launch_mode<64, kModePartial, false>(p, s) : launch_mode<64, kModeMerge, true>(p, s);
   return mode == kModePartial ? launch_mode<128, kModePartial, false>(p, s) : launch_mode<128, kModeMerge, true>(p, s);
+}
+
+bool fin_supported(int dtype, int head_dim, const AttnParams& p) {
+  const bool shape = (p.waves == 8 && p.ksplit == 1) || (p.waves == 8 && p.ksplit == 2) ||
+                     (p.waves == 4 && p.ksplit == 1);
+  return dtype == FB_BF16 && head_dim == 128 && shape && p.row_tiles == 1 && p.tiles == nullptr &&
+         p.dyn.groups == 0 && p.int_count > 0;
+}
+
+hipError_t launch_attn_fin(const AttnParams& p, const FinParams& f, hipStream_t s) {
+  if (!fin_supported(FB_BF16, 128, p) || f.cp.splits > 32) return hipErrorNotSupported;
+  if (p.waves == 8 && p.ksplit == 1) return launch_fin_batch<128, 8, 1>(p, f, s);
+  if (p.waves == 8 && p.ksplit == 2) return launch_fin_batch<128, 4, 2>(p, f, s);
+  return launch_fin_batch<128, 4, 1>(p, f, s);
 }
 
 }  // namespace fbk

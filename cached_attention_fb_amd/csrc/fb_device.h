@@ -120,13 +120,15 @@ struct AttnItem {
   bool ok;
   bool internal;   // a fused step's block-internal item
 };
-__device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial) {
+// bid: the item's index in the launch (the workgroup index, or the ticket of
+// a single-launch fused step), nblocks: the launch's attention items.
+__device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial, int bid, int nblocks) {
   AttnItem it;
   it.internal = false;
   int kps = p.keys_per_split;
   const int int_count = partial ? p.int_count : 0;
-  if ((int)blockIdx.x < int_count) {   // a fused step's block-internal item (they come first)
-    const int w = xcd_remap(blockIdx.x, int_count);
+  if (bid < int_count) {   // a fused step's block-internal item (they come first)
+    const int w = xcd_remap(bid, int_count);
     const int w1 = div_index(w, p.row_tiles, p.dv_row_tiles);
     it.rt = w - w1 * p.row_tiles;
     it.b = div_index(w1, p.hkv, p.dv_hkv);
@@ -138,7 +140,7 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
     it.internal = true;
     return it;
   }
-  const int w0 = (int)blockIdx.x - int_count;   // index among the external items
+  const int w0 = bid - int_count;   // index among the external items
   if (partial && p.dyn.groups > 0) {
     const uint64_t mask = active_groups(p.sel, p.dyn.groups, p.hq, p.hkv);
     const int n = __builtin_popcountll(mask);
@@ -159,7 +161,7 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
     const int tiles = (p.n_keys + kKeyTile - 1) / kKeyTile;
     kps = ((tiles + splits - 1) / splits) * kKeyTile;
   } else {
-    int w = xcd_remap(w0, (int)gridDim.x - int_count);
+    int w = xcd_remap(w0, nblocks - int_count);
     int q = div_index(w, p.row_tiles, p.dv_row_tiles);
     it.rt = w - q * p.row_tiles;
     w = q;
@@ -189,6 +191,10 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
   it.key_begin = it.split * kps;
   it.key_end = min(p.n_keys, it.key_begin + kps);
   return it;
+}
+
+__device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial) {
+  return attn_item(p, partial, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Work item of a merge launch on a 3-D grid (x: row tile, y: kv head, z:

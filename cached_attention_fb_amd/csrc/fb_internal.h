@@ -138,6 +138,31 @@ struct CombineParams {
   const int32_t* cum_m;
 };
 
+// Single-launch fused step: the split attention items, the block-internal
+// items and the split combine share one grid.  Workgroups below n_attn take
+// the attention items (by index, as in the two-launch form, XCD placement
+// included); the others take combine work, waiting (bounded) until every
+// attention workgroup of their group has arrived.  Each XCD dispatches its
+// workgroups in increasing index order, so a waiting combine workgroup only
+// ever waits for attention workgroups that are running or will be dispatched
+// once the attention workgroups ahead of them, which never wait, finish: the
+// wait needs no co-resident grid.  A group's last combine workgroup returns
+// its counter to zero, so a launch can be captured and replayed.
+struct FinParams {
+  CombineParams cp;
+  // counter i at ctr[i * kFinStride] (one 128-byte line each): 0 error flag
+  // (a combine workgroup gave up waiting), 1 + group: arrivals of group
+  // b*Hkv + g
+  uint32_t* ctr;
+  int32_t n_attn;         // attention workgroups: indexes 0 .. n_attn-1
+  int32_t n_total;        // + combine workgroups
+  int32_t chunks;         // combine workgroups per query head (256/D rows per wave)
+  uint32_t need;          // arrivals that complete a group (its attention items)
+  uint32_t done_all;      // need + the group's combine workgroups: the last one resets the counter
+};
+constexpr int kFinCounters = 1;   // counters before the per-group ones
+constexpr int kFinStride = 32;    // uint32 per counter
+
 // Tile list of the prefix keys a sparse selection leaves out.
 struct ComplementParams {
   const int32_t* sel;     // [groups][n_sel]
@@ -167,6 +192,8 @@ struct ResetParams {
   uint8_t* valid;
   uint8_t* reuse;         // [2][B*Hq]
   float* sim;
+  uint32_t* fin_ctr;      // the single-launch step's counters (zeroed), or null
+  int32_t fin_n;
 };
 
 enum AttnMode { kModePartial = 0, kModeMerge = 1 };
@@ -174,6 +201,10 @@ enum AttnMode { kModePartial = 0, kModeMerge = 1 };
 // Launchers (fb_aux.hip; launch_attn dispatches to the attention kernel files).
 // Return the launch status.
 hipError_t launch_attn(int dtype, int head_dim, int mode, const AttnParams& p, hipStream_t s);
+// The single-launch fused step (bf16, head dim 128, one row tile per group,
+// dense keys, host decisions); hipErrorNotSupported for other launches.
+hipError_t launch_attn_fin(const AttnParams& p, const FinParams& f, hipStream_t s);
+bool fin_supported(int dtype, int head_dim, const AttnParams& p);
 hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s);
 hipError_t launch_decide(const DecideParams& p, hipStream_t s);
 hipError_t launch_reset(const ResetParams& p, hipStream_t s);

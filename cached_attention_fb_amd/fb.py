@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfb.so")
 FB_OK, FB_E_ARG, FB_E_SHAPE, FB_E_DTYPE, FB_E_STATE, FB_E_NOMEM, FB_E_HIP, FB_E_UNSUPPORTED = range(8)
 FB_F32, FB_BF16 = 0, 1
 POLICY_ALWAYS, POLICY_TAU, POLICY_GAMMA, POLICY_TAU_CUM, POLICY_GAMMA_GROUP = 0, 1, 2, 3, 4
-FIELD_A_OUT, FIELD_L_OUT, FIELD_SIM, FIELD_REUSE, FIELD_VALID = range(5)
+FIELD_A_OUT, FIELD_L_OUT, FIELD_SIM, FIELD_REUSE, FIELD_VALID, FIELD_WAIT_ERR = range(6)
 PROFILE_KINDS = 8
 KIND_NAMES = ["external", "combine", "internal_merge", "decide", "reset", "sparse_kept", "sparse_total",
               "sparse_complement"]
@@ -240,7 +240,7 @@ class Cache:
         shape, dt = {FIELD_A_OUT: (nh + (c.block_size, c.head_dim), np.float32),
                      FIELD_L_OUT: (nh + (c.block_size,), np.float32),
                      FIELD_SIM: (nh, np.float32), FIELD_REUSE: (nh, np.uint8),
-                     FIELD_VALID: (nh, np.uint8)}[field]
+                     FIELD_VALID: (nh, np.uint8), FIELD_WAIT_ERR: ((1,), np.uint32)}[field]
         buf = np.empty(shape, dtype=dt)
         _check(self.lib.fb_cache_read(self.h, field, buf.ctypes.data, buf.nbytes, _stream(stream)))
         return buf

@@ -79,7 +79,10 @@ enum {
   FB_FIELD_L_OUT = 1,    /* float [B][Hq][Bs]     current cached L_out */
   FB_FIELD_SIM = 2,      /* float [B][Hq]         last similarity per head (NaN: none yet) */
   FB_FIELD_REUSE = 3,    /* uint8 [B][Hq]         1 if the head reused at the last fb_step */
-  FB_FIELD_VALID = 4     /* uint8 [B][Hq]         1 if the head's cache holds a computed A_out */
+  FB_FIELD_VALID = 4,    /* uint8 [B][Hq]         1 if the head's cache holds a computed A_out */
+  FB_FIELD_WAIT_ERR = 5  /* uint32 [1]            nonzero once a single-launch step's combine gave up
+                            waiting for its attention items (a diagnostic: the wait is bounded,
+                            and the flag stays set until the next fb_cache_reset) */
 };
 
 #define FB_MAX_BATCH 1024     /* sequences per cache */
@@ -192,7 +195,13 @@ typedef struct {
  * The first step after a reset recomputes every head even when
  * fb_external_attn filled the cache since the reset.
  * The whole step is asynchronous on `stream` (GAMMA decisions and TAU
- * decisions from device counts stay on the device).  Errors: FB_E_ARG (null,
+ * decisions from device counts stay on the device).  Where some head
+ * recomputes, the split attention over the prefix and the block-internal
+ * attention run as one kernel launch and the split combine as a second; with
+ * FB_FIN=1 in the environment at fb_cache_alloc all three run as one launch
+ * where the decisions are made on the host, the dtype is bf16, the head dim
+ * 128 and the query rows of a kv head (query heads per kv head x block size)
+ * at most 256 (the same results; profiling counts it as external attention).  Errors: FB_E_ARG (null,
  * bad policy, tau < 0, n_updated null under TAU, a negative n_updated),
  * FB_E_SHAPE, FB_E_STATE (prefix_len, policy or the host/device choice
  * differs from the previous step of the same block).

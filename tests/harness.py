@@ -24,6 +24,7 @@ class GpuBlock:
     l_out: np.ndarray    # [S, B, Hq, Bs]
     reuse: np.ndarray    # [S, B, Hq] uint8
     sim: np.ndarray      # [S, B, Hq]
+    wait_err: int = 0    # the single-launch step's wait error flag at block end
 
 
 def tolerance_check(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str, rel: bool = True) -> float:
@@ -114,6 +115,7 @@ def run_gpu(inp: wl.Inputs, policy: Optional[str] = None, kv_splits: int = 0,
                 g.a_out[s] = cache.read(fb.FIELD_A_OUT)
                 g.l_out[s] = cache.read(fb.FIELD_L_OUT)
                 g.sim[s] = cache.read(fb.FIELD_SIM)
+        g.wait_err = int(cache.read(fb.FIELD_WAIT_ERR)[0])
         res.append(g)
         # block end: the final block K/V join the prefix
         last = blk.steps[-1]
@@ -147,6 +149,7 @@ def compare_block(gpu: GpuBlock, ref: oracle.BlockResult, dtype: str, pairs=None
     by default every head maps to itself.  Per-step outputs are also checked
     relative to the largest reference magnitude of the compared heads."""
     errs = {"out": 0.0, "a_out": 0.0, "l_out": 0.0}
+    assert gpu.wait_err == 0, f"{what} a single-launch step gave up waiting for its attention items"
     S = ref.reuse.shape[0]
     if pairs is None:
         pairs = [((b, h), (b, h)) for b in range(ref.reuse.shape[1]) for h in range(ref.reuse.shape[2])]
