@@ -503,10 +503,22 @@ __device__ __forceinline__ void fin_combine(const FinParams& f, int c) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int bh = c / f.chunks, chunk = c - bh * f.chunks;
   const int b = bh / p.hq, h = bh - b * p.hq;
-  uint32_t* cnt = f.ctr + (kFinCounters + b * p.hkv + h / (p.hq / p.hkv)) * kFinStride;
+  const int gi = b * p.hkv + h / (p.hq / p.hkv);
+  uint32_t* cnt = f.ctr + (kFinCounters + gi) * kFinStride;
+  uint32_t need = f.need, done_all = f.done_all;
+  if (p.dyn.groups > 0) {   // the device plan: what the attention workgroups derived, from the same flags
+    const uint64_t mask = active_groups(p.sel, p.dyn.groups, p.hq, p.hkv);
+    const bool act = (mask >> gi) & 1;
+    if (f.merge_reused && !act) return;   // the block-internal items finished the group
+    const int splits = act ? p.dyn.splits[__builtin_popcountll(mask)] : 0;
+    need = (uint32_t)((splits + 1) * f.row_tiles);
+    done_all = need + (uint32_t)((p.hq / p.hkv) * f.chunks);
+  } else if (f.merge_reused && !group_selected(p.sel, b, h / (p.hq / p.hkv), p.hq, p.hq / p.hkv)) {
+    return;
+  }
   if (threadIdx.x == 0) {
     for (int i = 0;; ++i) {
-      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= f.need) break;
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
       if (i == kFinSpin) {
         __hip_atomic_fetch_or(f.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -520,7 +532,7 @@ __device__ __forceinline__ void fin_combine(const FinParams& f, int c) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t o = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (o + 1 == f.done_all) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (o + 1 == done_all) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -531,8 +543,19 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_fin_kernel(const Attn
   if ((int)blockIdx.x < f.n_attn) {   // workgroup-uniform
     const AttnItem it = attn_item(p, true, blockIdx.x, f.n_attn);
     record_decisions(p);
+    // A group with no selected head (block-internal items; static-plan split
+    // items, which the device plan does not enumerate): its block-internal
+    // items merge with the cache and store the output, as the merge launch
+    // does; nothing waits for the group.
+    if (f.merge_reused && (it.internal || p.dyn.groups == 0) &&
+        !(it.internal ? group_selected(p.sel, it.b, it.g, p.hq, p.grp) : it.ok)) {
+      if (it.internal) attn_body<D, ROWW, KSPLIT, kModeMerge, false, false, AUX, false>(p, it);
+      return;
+    }
     if (it.ok) attn_body<D, ROWW, KSPLIT, kModePartial, false, false, AUX, false, true>(p, it);
-    fin_arrive(f, it.b * p.hkv + it.g);
+    // static plan: a group without a selected head still counts its items;
+    // device plan: the items past the active groups' belong to no group
+    if (it.ok || p.dyn.groups == 0) fin_arrive(f, it.b * p.hkv + it.g);
   } else {
     fin_combine<D, ROWW * KSPLIT, BATCH>(f, blockIdx.x - f.n_attn);
   }
@@ -600,8 +623,11 @@ hipError_t launch_fin(const AttnParams& p, const FinParams& f, hipStream_t s) {
 
 template <int D, int ROWW, int KSPLIT>
 hipError_t launch_fin_batch(const AttnParams& p, const FinParams& f, hipStream_t s) {
-  if (f.cp.splits <= 8) return launch_fin<D, ROWW, KSPLIT, 8>(p, f, s);
-  if (f.cp.splits <= 16) return launch_fin<D, ROWW, KSPLIT, 16>(p, f, s);
+  // the combine kernel's round size: the largest split count of the plan
+  int most = f.cp.splits;
+  for (int n = 1; n <= f.cp.dyn.groups; ++n) most = std::max(most, (int)f.cp.dyn.splits[n]);
+  if (most <= 8) return launch_fin<D, ROWW, KSPLIT, 8>(p, f, s);
+  if (most <= 16) return launch_fin<D, ROWW, KSPLIT, 16>(p, f, s);
   return launch_fin<D, ROWW, KSPLIT, 32>(p, f, s);
 }
 
@@ -661,11 +687,13 @@ bool fin_supported(int dtype, int head_dim, const AttnParams& p) {
   const bool shape = (p.waves == 8 && p.ksplit == 1) || (p.waves == 8 && p.ksplit == 2) ||
                      (p.waves == 4 && p.ksplit == 1);
   return dtype == FB_BF16 && head_dim == 128 && shape && p.row_tiles == 1 && p.tiles == nullptr &&
-         p.dyn.groups == 0 && p.int_count > 0;
+         p.int_count > 0;
 }
 
 hipError_t launch_attn_fin(const AttnParams& p, const FinParams& f, hipStream_t s) {
-  if (!fin_supported(FB_BF16, 128, p) || f.cp.splits > 32) return hipErrorNotSupported;
+  if (!fin_supported(FB_BF16, 128, p) || f.cp.splits > 32 || f.row_tiles != p.row_tiles ||
+      f.cp.dyn.groups != p.dyn.groups)
+    return hipErrorNotSupported;
   if (p.waves == 8 && p.ksplit == 1) return launch_fin_batch<128, 8, 1>(p, f, s);
   if (p.waves == 8 && p.ksplit == 2) return launch_fin_batch<128, 4, 2>(p, f, s);
   return launch_fin_batch<128, 4, 1>(p, f, s);

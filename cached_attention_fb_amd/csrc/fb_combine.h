@@ -266,7 +266,7 @@ __device__ __forceinline__ void combine_fold(const CombineParams& p, int ch, int
       t[2] = no;
     }
   }
-  if (sel && !p.sim_terms && !tot && ch == 0 && tid == 0) p.valid[bh] = 1;
+  if (sel && !p.sim_terms && !tot && !p.keep_valid && ch == 0 && tid == 0) p.valid[bh] = 1;
 }
 
 }  // namespace

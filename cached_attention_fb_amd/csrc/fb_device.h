@@ -79,6 +79,13 @@ __device__ __forceinline__ bool head_selected(const HeadSel& s, int b, int bh) {
   return (s.flags[bh] != 0) == (s.flags_select != 0);
 }
 
+// Whether any query head of group (b, g) is selected.
+__device__ __forceinline__ bool group_selected(const HeadSel& s, int b, int g, int hq, int grp) {
+  bool any = false;
+  for (int i = 0; i < grp; ++i) any |= head_selected(s, b, b * hq + g * grp + i);
+  return any;
+}
+
 // Partial launches whose heads are decided in the kernel: the first workgroup
 // records 1 - selected for every head, which the launches after it select
 // from (they may change what the decision reads).  Runs before any early exit.
@@ -181,9 +188,7 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial,
         // decided per sequence (the host's threshold decisions): no head loop
         any = p.sel.every_seq || ((p.sel.seq_bits[it.b >> 5] >> (it.b & 31)) & 1u);
       } else {
-        const int grp = p.grp;
-        any = false;
-        for (int i = 0; i < grp; ++i) any |= head_selected(p.sel, it.b, it.b * p.hq + it.g * grp + i);
+        any = group_selected(p.sel, it.b, it.g, p.hq, p.grp);
       }
       it.ok = any;
     }

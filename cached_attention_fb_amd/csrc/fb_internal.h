@@ -136,6 +136,9 @@ struct CombineParams {
   // head of b was selected (recomputed), else grows by cum_m[b]
   int32_t* cum;
   const int32_t* cum_m;
+  // 1: a recomputed head's valid flag is left as it is (a single-launch step
+  // whose workgroups read the flags for their decisions while others fold)
+  int32_t keep_valid;
 };
 
 // Single-launch fused step: the split attention items, the block-internal
@@ -159,6 +162,17 @@ struct FinParams {
   int32_t chunks;         // combine workgroups per query head (256/D rows per wave)
   uint32_t need;          // arrivals that complete a group (its attention items)
   uint32_t done_all;      // need + the group's combine workgroups: the last one resets the counter
+  // With a device plan (cp.dyn.groups > 0) the two counts above are taken in
+  // the kernel from the active groups instead: a group then has
+  // (dyn.splits[n] + 1) * row_tiles attention items if active, row_tiles (its
+  // block-internal ones) if not, and the workgroups past the plan's items
+  // belong to no group and do not arrive.
+  int32_t row_tiles;
+  // 1: a group with no selected head is finished by its block-internal items
+  // alone (the merge launch's epilogue: the cached part folded in, the output
+  // stored; AttnParams' merge fields are set); its split items and its
+  // combine workgroups exit at once and nothing counts on its counter.
+  int32_t merge_reused;
 };
 constexpr int kFinCounters = 1;   // counters before the per-group ones
 constexpr int kFinStride = 32;    // uint32 per counter

@@ -125,7 +125,8 @@ struct fb_cache {
   // (FinParams); null where the step keeps its two launches
   uint32_t* fin_ctr = nullptr;
   int fin_n = 0;
-  bool fin_on = false;    // FB_FIN=1 at allocation: the single-launch step (measured no faster)
+  // single-launch steps: FB_FIN=1 at allocation (measured no faster)
+  bool fin_on = false;
   int64_t part_o_stride_override = 0;   // > 0: distance of the partials' slots in elements (caller scratch)
   int64_t part_l_stride_override = 0;
   int comp_stride = 1;       // ceil(max_prefix / 64), at least 1
@@ -370,6 +371,10 @@ struct ExtOpts {
   const void* vblk = nullptr;
   void* out = nullptr;
   const int32_t* cum_m = nullptr;   // cumulative threshold decided on the device
+  // threshold decided on the device at a step after the block's first: every
+  // head's valid flag is already set, so the step may run as one launch
+  // whose workgroups each evaluate the rule (see run_external)
+  bool fin_dev = false;
 };
 
 // External attention over a key set for the heads `sel` selects, and the
@@ -451,11 +456,20 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   cp.bs = c->cfg.block_size;
   cp.row_chunks = c->row_chunks;
   cp.sel = sel;
-  if (o.rec != nullptr && o.follow_rec) {
+  // A threshold step decided on the device after the block's first may run
+  // as one launch (below, opt-in): every workgroup, the combine's included, evaluates
+  // the rule from flags that no workgroup of the launch changes (the valid
+  // flags are all set after the block's first step, and the combine leaves
+  // them alone), so they all see the same decisions and the same plan.
+  const bool fin_dev = o.fin_dev && c->fin_ctr != nullptr && c->fin_on && fused && !o.to_total &&
+                       o.cum_m == nullptr && sel.flags == nullptr && sel.m != nullptr && ext_items > 0 &&
+                       fbk::fin_supported(c->cfg.dtype, c->cfg.head_dim, p);
+  if (o.rec != nullptr && o.follow_rec && !fin_dev) {
     cp.sel = all_heads(c);
     cp.sel.flags = o.rec;
     cp.sel.flags_select = 0;
   }
+  cp.keep_valid = fin_dev ? 1 : 0;
   cp.slot_o = c->slot_o;
   cp.slot_l = c->slot_l;
   cp.valid = c->valid;
@@ -474,14 +488,20 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
     cp.cum = c->cum;
     cp.cum_m = o.cum_m;
   }
-  // One launch for the whole step (opt-in, where the kernels allow it): the
-  // split and block-internal items and the combine share a grid (FinParams).
-  // Bitwise the same results; measured no faster than the two launches
-  // (dllm-8k 19.5 against 18.2 us per recompute step, long and max within
-  // 1 %), so the two launches stay the default.
-  const bool fin = c->fin_ctr != nullptr && c->fin_on && fused && !o.to_total && o.cum_m == nullptr &&
-                   !(o.rec != nullptr && o.follow_rec) && ext_items > 0 && sel.flags == nullptr &&
-                   sel.m == nullptr && p.splits <= 32 && fbk::fin_supported(c->cfg.dtype, c->cfg.head_dim, p);
+  // One launch for the whole step (opt-in, FB_FIN=1): the split and
+  // block-internal items and the combine share a grid (FinParams); a group
+  // whose heads all reuse is finished by its block-internal items.  The same
+  // caches and decisions, and the same outputs for recomputed heads, as the
+  // two launches.  Measured no faster: dllm-8k 19.5 against 18.2 us per
+  // recompute step (long and max within 1 %); with device decisions a step
+  // in which every head reuses still takes 9.5-10 us, most of it the
+  // block-internal workgroup's own chain of dependent steps (parameters,
+  // loads, one key tile, the merge: 8.3 us, against 2.9 us for a workgroup
+  // of the lone-wave merge launch), so the two launches stay the default.
+  const bool fin = fin_dev || (c->fin_ctr != nullptr && c->fin_on && fused && !o.to_total &&
+                                o.cum_m == nullptr && !(o.rec != nullptr && o.follow_rec) && ext_items > 0 &&
+                                sel.flags == nullptr && sel.m == nullptr &&
+                                fbk::fin_supported(c->cfg.dtype, c->cfg.head_dim, p));
   ProfRec r;
   hipError_t e = hipSuccess;
   if (fin) {
@@ -492,8 +512,15 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
     f.chunks = (c->row_chunks + p.waves - 1) / p.waves;
     f.n_total = p.grid + c->cfg.batch * c->cfg.n_q_heads * f.chunks;
     const int grp = c->cfg.n_q_heads / c->cfg.n_kv_heads;
-    f.need = (uint32_t)((p.splits + 1) * p.row_tiles);
+    f.need = (uint32_t)((p.splits + 1) * p.row_tiles);   // static plan; a device plan counts in the kernel
     f.done_all = f.need + (uint32_t)(grp * f.chunks);
+    f.row_tiles = p.row_tiles;
+    // groups that reuse are finished by their block-internal items
+    f.merge_reused = 1;
+    p.slot_o = c->slot_o;
+    p.slot_l = c->slot_l;
+    p.valid = c->valid;
+    p.out = o.out;
     prof_begin(c, s, &r, 0);
     e = fbk::launch_attn_fin(p, f, s);
     prof_end(c, s, &r);
@@ -903,6 +930,7 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const fb_step_opts* o
     ext_active = groups;
     eo.rec = reuse_now;
     if (pa->policy == FB_POLICY_TAU_CUM) eo.cum_m = n_updated_dev;
+    eo.fin_dev = c->steps > 0 && pa->policy == FB_POLICY_TAU;
   } else {
     ext_sel.flags = nullptr;
     ext_sel.flags_select = 1;

@@ -197,11 +197,16 @@ typedef struct {
  * The whole step is asynchronous on `stream` (GAMMA decisions and TAU
  * decisions from device counts stay on the device).  Where some head
  * recomputes, the split attention over the prefix and the block-internal
- * attention run as one kernel launch and the split combine as a second; with
+ * attention run as one kernel launch and the split combine as a second.  With
  * FB_FIN=1 in the environment at fb_cache_alloc all three run as one launch
- * where the decisions are made on the host, the dtype is bf16, the head dim
- * 128 and the query rows of a kv head (query heads per kv head x block size)
- * at most 256 (the same results; profiling counts it as external attention).  Errors: FB_E_ARG (null,
+ * (profiling counts it as external attention) where the dtype is bf16, the
+ * head dim 128 and the query rows of a kv head (query heads per kv head x
+ * block size) at most 256, and the decisions are made on the host or are TAU
+ * decisions from device counts after the block's first step: the same cache
+ * and decisions, and the same outputs for recomputed heads; a kv head whose
+ * query heads all reuse then takes its output from the block-internal
+ * attention's merge, within one output rounding of the two launches'.
+ * Errors: FB_E_ARG (null,
  * bad policy, tau < 0, n_updated null under TAU, a negative n_updated),
  * FB_E_SHAPE, FB_E_STATE (prefix_len, policy or the host/device choice
  * differs from the previous step of the same block).
