@@ -541,7 +541,7 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_fin_kernel(const Attn
   prefetch_params(p);
   prefetch_params(f);
   if ((int)blockIdx.x < f.n_attn) {   // workgroup-uniform
-    const AttnItem it = attn_item(p, true, blockIdx.x, f.n_attn);
+    const AttnItem it = attn_item<false>(p, true, blockIdx.x, f.n_attn);   // dense keys only
     record_decisions(p);
     // A group with no selected head (block-internal items; static-plan split
     // items, which the device plan does not enumerate): its block-internal

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_r64_kernel(const AttnParams 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rw = wave % kRowW, kh = wave / kRowW;
   const int rl = lane & 31, hl = lane >> 5;
-  const AttnItem it = attn_item(p, true);
+  const AttnItem it = attn_item<false>(p, true);   // dense keys only
   record_decisions(p);
   if (!it.ok) return;   // workgroup-uniform
   const int b = it.b, g = it.g, grp = p.grp;

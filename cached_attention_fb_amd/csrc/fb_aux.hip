@@ -66,13 +66,6 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(const DecideParams p) 
   }
 }
 
-// Per-head decisions made on the host, recorded for a step that launches no
-// attention over them: 1 - selected.
-__global__ __launch_bounds__(kThreads) void record_kernel(const HeadSel sel, uint8_t* rec, int n_heads, int hq) {
-  const int bh = blockIdx.x * kThreads + threadIdx.x;
-  if (bh < n_heads) rec[bh] = head_selected(sel, bh / hq, bh) ? 0 : 1;
-}
-
 __global__ __launch_bounds__(kThreads) void reset_kernel(const ResetParams p) {
   const int bh = blockIdx.x * kThreads + threadIdx.x;
   if (p.fin_ctr != nullptr && bh < p.fin_n) p.fin_ctr[bh] = 0;
@@ -148,6 +141,7 @@ hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s) {
   // largest split count this launch can see (the device plan's too)
   int most = p.splits;
   for (int n = 1; n <= p.dyn.groups; ++n) most = std::max(most, (int)p.dyn.splits[n]);
+  if (p.two_sets) most = std::max(most, (int)p.splits2);
   if (p.part_bf16) {
     if (head_dim == 64) return launch_combine_batch<64, true>(most, blocks, p, s);
     return launch_combine_batch<128, true>(most, blocks, p, s);
@@ -166,12 +160,6 @@ hipError_t launch_combine_batch(int most, dim3 blocks, const CombineParams& p, h
 
 hipError_t launch_decide(const DecideParams& p, hipStream_t s) {
   hipLaunchKernelGGL(decide_kernel, dim3(p.n_heads), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_record(const HeadSel& sel, uint8_t* rec, int n_heads, int hq, hipStream_t s) {
-  hipLaunchKernelGGL(record_kernel, dim3((n_heads + kThreads - 1) / kThreads), dim3(kThreads), 0, s, sel, rec, n_heads,
-                     hq);
   return hipGetLastError();
 }
 

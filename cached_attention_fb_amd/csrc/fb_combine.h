@@ -20,7 +20,10 @@ namespace {
 // gamma, before replacing each cached value it sums <A_new, A_old>, |A_new|^2
 // and |A_old|^2 over its rows for the similarity.  In total mode (sparse attention: the
 // splits are the kept keys) the fold starts from the head's cached part and
-// the result goes to the total buffer.
+// the result goes to the total buffer.  With two key sets (a sparse step in
+// which some head recomputes) a selected head's splits of the first set
+// (the left-out keys) refresh its cache, and then every head folds the
+// second set's splits (the kept keys) onto its cached part.
 // One float4 column of a partial A: fp32, or bf16 widened.
 template <bool PB>
 __device__ __forceinline__ f32x4 load_part(const float* base, int64_t off) {
@@ -126,6 +129,7 @@ __device__ __forceinline__ void combine_fold(const CombineParams& p, int ch, int
   constexpr int kRows = kCombineThreads / kLpr;
   const bool out_mode = p.out != nullptr;
   const bool sel = head_selected(p.sel, b, bh);
+  const bool two = p.two_sets != 0;
   if (p.cum != nullptr && bh % p.hq == 0 && ch == 0 && tid == 0) {   // once per sequence
     bool any = false;
     for (int h = 0; h < p.hq; ++h) any |= head_selected(p.sel, b, b * p.hq + h);
@@ -150,7 +154,7 @@ __device__ __forceinline__ void combine_fold(const CombineParams& p, int ch, int
     f32x4 acc = {0, 0, 0, 0};
     // the cached part enters as one more term, normalised (weight 1 at its
     // max): in total mode, and for the output of a head that reuses it
-    if ((tot || !sel) && p.valid[bh] != 0) {
+    if ((two ? !sel : (tot || !sel)) && p.valid[bh] != 0) {
       const float l0 = p.slot_l[grow];
       if (l0 > -INFINITY) {
         mx = l0;
@@ -176,19 +180,21 @@ __device__ __forceinline__ void combine_fold(const CombineParams& p, int ch, int
     // operations, see group_max).  Every lane still adds the
     // splits' A in split order.
     constexpr int kLl = (BATCH + kLpr - 1) / kLpr;   // L values per lane and round
-    for (int s = 0; s < splits; s += BATCH) {
+    // the splits first .. first + count - 1, folded into (mx, wsum, acc)
+    auto fold = [&](int first, int count) {
+    for (int s = 0; s < count; s += BATCH) {
       float lv[kLl];
       PartRaw<PB> a[BATCH];   // widened where used: a conversion here would wait for its load
 #pragma unroll
       for (int k = 0; k < kLl; ++k) {
         const int u = c4 + kLpr * k;
-        const int si = min(s + u, splits - 1);
+        const int si = first + min(s + u, count - 1);
         lv[k] = load_l<COH>(lp + si * p.part_l_stride);
-        if (u >= BATCH || s + u >= splits) lv[k] = -INFINITY;
+        if (u >= BATCH || s + u >= count) lv[k] = -INFINITY;
       }
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
-        const int si = min(s + u, splits - 1);
+        const int si = first + min(s + u, count - 1);
         a[u] = load_part_raw<PB, COH>(p.part_o, ao + si * p.part_o_stride);
       }
       // keep every load of the round ahead of the arithmetic: left to itself
@@ -218,6 +224,8 @@ __device__ __forceinline__ void combine_fold(const CombineParams& p, int ch, int
         mx = nm;
       }
     }
+    };
+    fold(0, splits);
     if (sel && !(tot && out_mode)) {   // a recomputed head's new value: into the cache (total mode: the buffer)
       const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
       const f32x4 a_new = acc * inv;
@@ -235,7 +243,14 @@ __device__ __forceinline__ void combine_fold(const CombineParams& p, int ch, int
       float* ld = (tot ? p.tot_l : p.slot_l) + grow;
       *reinterpret_cast<f32x4*>(od + 4 * c4) = a_new;
       if (c4 == 0) *ld = lse;
+      if (two) {   // the total starts from the cached part just stored, as a read of it would
+        const bool has = lse > -INFINITY;
+        mx = has ? lse : -INFINITY;
+        wsum = has ? 1.0f : 0.0f;
+        acc = has ? a_new : f32x4{0, 0, 0, 0};
+      }
     }
+    if (two) fold(p.base2, p.splits2);   // the second key set (kept keys), every head
     if (out_mode) {   // the block-internal part (page §2 merge), then the step's output
       const f32x4 a_in = widen_part<PB>(a_in_raw);
       const float nm = fmaxf(mx, l_in);

@@ -93,7 +93,7 @@ __device__ __forceinline__ void record_decisions(const AttnParams& p) {
   if (p.reuse_rec == nullptr || blockIdx.x != 0) return;
   const int nh = p.batch * p.hq;
   for (int bh = threadIdx.x; bh < nh; bh += blockDim.x)
-    p.reuse_rec[bh] = head_selected(p.sel, bh / p.hq, bh) ? 0 : 1;
+    p.reuse_rec[bh] = (p.rec_reuse_all || !head_selected(p.sel, bh / p.hq, bh)) ? 1 : 0;
 }
 
 
@@ -126,12 +126,16 @@ struct AttnItem {
   int key_begin, key_end;
   bool ok;
   bool internal;   // a fused step's block-internal item
+  bool seg2;       // an item of the launch's second key set
 };
 // bid: the item's index in the launch (the workgroup index, or the ticket of
 // a single-launch fused step), nblocks: the launch's attention items.
+// TWO_SETS = false: a kernel never launched with a second key set.
+template <bool TWO_SETS = true>
 __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial, int bid, int nblocks) {
   AttnItem it;
   it.internal = false;
+  it.seg2 = false;
   int kps = p.keys_per_split;
   const int int_count = partial ? p.int_count : 0;
   if (bid < int_count) {   // a fused step's block-internal item (they come first)
@@ -148,6 +152,23 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial,
     return it;
   }
   const int w0 = bid - int_count;   // index among the external items
+  const int seg2_items = TWO_SETS && partial ? p.seg2_items : 0;
+  const int n1 = nblocks - int_count - seg2_items;   // the first key set's items
+  if (TWO_SETS && w0 >= n1) {   // the second key set: every group, a static plan
+    int w = xcd_remap(w0 - n1, seg2_items);
+    it.rt = w % p.row_tiles;
+    w /= p.row_tiles;
+    const int split = w % p.seg2_splits;
+    w /= p.seg2_splits;
+    it.b = w / p.hkv;
+    it.g = w % p.hkv;
+    it.key_begin = split * p.seg2_kps;
+    it.key_end = min(p.n_keys2, it.key_begin + p.seg2_kps);
+    it.split = p.seg2_base + split;
+    it.ok = true;
+    it.seg2 = true;
+    return it;
+  }
   if (partial && p.dyn.groups > 0) {
     const uint64_t mask = active_groups(p.sel, p.dyn.groups, p.hq, p.hkv);
     const int n = __builtin_popcountll(mask);
@@ -168,7 +189,7 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial,
     const int tiles = (p.n_keys + kKeyTile - 1) / kKeyTile;
     kps = ((tiles + splits - 1) / splits) * kKeyTile;
   } else {
-    int w = xcd_remap(w0, nblocks - int_count);
+    int w = xcd_remap(w0, n1);
     int q = div_index(w, p.row_tiles, p.dv_row_tiles);
     it.rt = w - q * p.row_tiles;
     w = q;
@@ -198,8 +219,9 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial,
   return it;
 }
 
+template <bool TWO_SETS = true>
 __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial) {
-  return attn_item(p, partial, (int)blockIdx.x, (int)gridDim.x);
+  return attn_item<TWO_SETS>(p, partial, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Work item of a merge launch on a 3-D grid (x: row tile, y: kv head, z:
@@ -207,6 +229,7 @@ __device__ __forceinline__ AttnItem attn_item(const AttnParams& p, bool partial)
 __device__ __forceinline__ AttnItem grid_item(const AttnParams& p) {
   AttnItem it;
   it.internal = false;
+  it.seg2 = false;
   it.rt = blockIdx.x;
   it.g = blockIdx.y;
   it.b = blockIdx.z;
@@ -251,13 +274,14 @@ template <bool MAYBE_LIST>
 __device__ __forceinline__ TileMap<MAYBE_LIST> tile_map(const AttnParams& p, const AttnItem& it) {
   TileMap<MAYBE_LIST> m;
   const int b = it.b, g = it.g, key_begin = it.key_begin, key_end = it.key_end;
-  if (!MAYBE_LIST || p.tiles == nullptr || it.internal) {
+  const int32_t* tiles = it.seg2 ? p.tiles2 : p.tiles;
+  if (!MAYBE_LIST || tiles == nullptr || it.internal) {
     m.list = nullptr;
     m.key_begin = key_begin;
     m.lim = key_end;
     m.phys_tiles = 0;
   } else {
-    m.list = p.tiles + ((int64_t)b * p.hkv + g) * p.tiles_stride + key_begin / kKeyTile;
+    m.list = tiles + ((int64_t)b * p.hkv + g) * (it.seg2 ? p.tiles2_stride : p.tiles_stride) + key_begin / kKeyTile;
     m.key_begin = 0;
     m.lim = p.n_phys;
     m.phys_tiles = (p.n_phys + kKeyTile - 1) / kKeyTile;

@@ -100,6 +100,17 @@ struct AttnParams {
   // [B][Hq] or null: 1 - selected(b, h) is recorded (merge: by the head's own
   // rows; partial: every head, by the first workgroup, for the launches after)
   uint8_t* reuse_rec;
+  // A second key set (partial mode, tile lists on both sets): after the
+  // first set's items (whose plan the fields above give) come seg2_items
+  // items over list tiles2 (tiles2_stride entries per group, n_keys2 keys)
+  // for every group: seg2_splits ranges of seg2_kps keys each, whose
+  // partials go to split index seg2_base + range.
+  const int32_t* tiles2;
+  int32_t tiles2_stride, n_keys2, seg2_items, seg2_splits, seg2_kps, seg2_base;
+  // partial launches: 1 records reuse (1) for every head without evaluating
+  // sel (a step the host knows reuses everywhere, e.g. a sparse step's
+  // kept-key launch, whose sel selects every head)
+  int32_t rec_reuse_all;
 };
 
 struct CombineParams {
@@ -139,6 +150,11 @@ struct CombineParams {
   // 1: a recomputed head's valid flag is left as it is (a single-launch step
   // whose workgroups read the flags for their decisions while others fold)
   int32_t keep_valid;
+  // Two key sets (two_sets = 1; tot_o null, out set): splits 0 .. splits-1
+  // of a selected head are its first key set (they refresh the cache as
+  // usual); then every head folds splits base2 .. base2+splits2-1 (the
+  // second set) onto its cached part before the block-internal partial.
+  int32_t two_sets, splits2, base2;
 };
 
 // Single-launch fused step: the split attention items, the block-internal
@@ -223,7 +239,6 @@ hipError_t launch_combine(int head_dim, const CombineParams& p, hipStream_t s);
 hipError_t launch_decide(const DecideParams& p, hipStream_t s);
 hipError_t launch_reset(const ResetParams& p, hipStream_t s);
 hipError_t launch_complement(const ComplementParams& p, hipStream_t s);
-hipError_t launch_record(const HeadSel& sel, uint8_t* rec, int n_heads, int hq, hipStream_t s);
 
 // Sets the calling thread's error message (fb_last_error) and returns code.
 fb_status report(fb_status code, const char* msg);

@@ -269,6 +269,44 @@ int choose_splits(fb_cache* c, int n_keys, int active_groups, int co_items = 0, 
   return (tiles + tiles_per - 1) / tiles_per;   // no empty chunk
 }
 
+// Two key sets in one launch (a sparse step's left-out tiles for the groups1
+// groups that recompute, its kept tiles for every group): the first set's
+// chunk count when both are cut into chunks of the same length, taken as in
+// choose_splits (the fewest chunks within 2 % of the best makespan, the
+// block-internal workgroups included), with both sets' chunks together at
+// most the scratch capacity; 0 if no length fits.
+int choose_splits2(fb_cache* c, int t1, int groups1, int t2, int co_items, int co_tiles) {
+  const int hit = c->split_memo.find(t1, groups1, co_items, -1 - t2);   // (a key no one-set entry has)
+  if (hit >= 0) return hit;
+  const long g_all = (long)c->cfg.batch * c->cfg.n_kv_heads;
+  auto span = [&](int s1, int* e1_out) -> double {
+    const int per = (t1 + s1 - 1) / s1, e1 = (t1 + per - 1) / per, e2 = (t2 + per - 1) / per;
+    *e1_out = e1;
+    if (e1 + e2 > c->splits_cap) return -1.0;
+    const long items = ((long)groups1 * e1 + g_all * e2) * c->row_tiles;
+    if (co_items > 0) return (double)span_with_co_items(c->n_cu, co_items, co_tiles, items, per);
+    return (double)((items + c->n_cu - 1) / c->n_cu) * per;
+  };
+  const int smax = std::max(1, std::min(t1, c->splits_cap));
+  double best = 1e30;
+  int e1;
+  for (int s1 = 1; s1 <= smax; ++s1) {
+    const double v = span(s1, &e1);
+    if (v >= 0.0) best = std::min(best, v);
+  }
+  int pick = 0;
+  if (best < 1e30)
+    for (int s1 = 1; s1 <= smax; ++s1) {
+      const double v = span(s1, &e1);
+      if (v >= 0.0 && v <= 1.02 * best) {
+        pick = e1;
+        break;
+      }
+    }
+  c->split_memo.put(t1, groups1, co_items, -1 - t2, pick);
+  return pick;
+}
+
 // Profiling records HIP events, which stream capture would take into a graph.
 fb_status check_not_capturing_profiled(const fb_cache* c, hipStream_t s) {
   if (!c->prof) return FB_OK;
@@ -375,6 +413,14 @@ struct ExtOpts {
   // head's valid flag is already set, so the step may run as one launch
   // whose workgroups each evaluate the rule (see run_external)
   bool fin_dev = false;
+  bool rec_reuse_all = false;   // the attention launch records reuse for every head (rec, not followed)
+  // A second key set attended for every head in the same launch (sparse
+  // steps: the kept tiles), folded by the same combine onto each head's
+  // cached part before the block-internal part (fused steps only).  When its
+  // splits do not fit the partial buffer next to the first set's, nothing is
+  // launched and *set2_done is false.
+  const KeySet* set2 = nullptr;
+  bool* set2_done = nullptr;
 };
 
 // External attention over a key set for the heads `sel` selects, and the
@@ -417,13 +463,64 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   const bool skip_ext = o.to_total && n == 0;   // nothing kept: the total is the cached part
   if (skip_ext) ext_items = 0;
   p.ring_keys = p.keys_per_split;
-  p.grid = ext_items;
+  int seg2_items = 0;
+  if (o.set2 != nullptr) {
+    // The second set for every group, a static plan.  Where the host knows
+    // the first set's groups (static plan, or its own decisions), both sets
+    // are cut into items of one length chosen together (choose_splits2);
+    // with decisions made on the device, the second set's items take the
+    // first set's longest range.  Either way in as many ranges as the partial
+    // buffer has left after the first set's.
+    const KeySet& k2 = *o.set2;
+    const int G = c->cfg.batch * c->cfg.n_kv_heads;
+    const int tiles2 = (k2.n_keys + fbk::kKeyTile - 1) / fbk::kKeyTile;
+    const bool dev_dyn = p.dyn.groups > 0 && (sel.flags != nullptr || sel.m != nullptr);
+    int base2 = p.splits, s2 = -1;
+    if (!dev_dyn && n > 0 && tiles2 > 0 && c->kv_splits == 0) {
+      const int A = p.dyn.groups > 0 ? active_groups : G;
+      const int s1 = choose_splits2(c, tiles, A, tiles2, co_items, co_tiles);
+      if (s1 > 0) {
+        const int per = (tiles + s1 - 1) / s1;
+        if (p.dyn.groups > 0) {
+          p.dyn.splits[A] = (uint8_t)s1;   // the host's own decisions select A groups
+          p.keys_per_split = std::max(p.keys_per_split, per * fbk::kKeyTile);   // LDS sizing: the longest range
+        } else {
+          p.splits = s1;
+          p.keys_per_split = per * fbk::kKeyTile;
+        }
+        ext_items = A * p.row_tiles * s1;
+        base2 = s1;
+        s2 = (tiles2 + per - 1) / per;
+      }
+    }
+    if (s2 < 0) {
+      for (int g = 1; g <= p.dyn.groups; ++g) base2 = std::max(base2, (int)p.dyn.splits[g]);
+      const int kps_tiles = std::max(1, p.keys_per_split / fbk::kKeyTile);
+      s2 = std::min((tiles2 + kps_tiles - 1) / kps_tiles, c->splits_cap - base2);
+    }
+    if (!fused || (tiles2 > 0 && s2 < 1)) {
+      if (o.set2_done) *o.set2_done = false;
+      return FB_OK;
+    }
+    if (o.set2_done) *o.set2_done = true;
+    p.tiles2 = k2.tiles;
+    p.tiles2_stride = k2.stride;
+    p.n_keys2 = k2.n_keys;
+    p.seg2_splits = s2;
+    p.seg2_kps = s2 > 0 ? std::max(1, (tiles2 + s2 - 1) / s2) * fbk::kKeyTile : fbk::kKeyTile;
+    p.seg2_base = base2;
+    seg2_items = G * s2 * p.row_tiles;
+    p.seg2_items = seg2_items;
+    p.ring_keys = std::max(p.ring_keys, p.keys_per_split);
+    if (s2 > 0) p.ring_keys = std::max(p.ring_keys, p.seg2_kps);
+  }
+  p.grid = ext_items + seg2_items;
   if (fused) {
     p.kblk = o.kblk;
     p.vblk = o.vblk;
     p.int_count = c->cfg.batch * c->cfg.n_kv_heads * p.row_tiles;
     p.int_split = c->splits_cap;
-    p.grid = ext_items + p.int_count;
+    p.grid = ext_items + seg2_items + p.int_count;
     p.ring_keys = std::max(p.ring_keys, ((c->cfg.block_size + fbk::kKeyTile - 1) / fbk::kKeyTile) * fbk::kKeyTile);
   }
   // Short work items (few tiles each, as at dLLM prefix lengths) run one
@@ -438,6 +535,7 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   }
   p.sel = sel;
   p.reuse_rec = o.rec;
+  p.rec_reuse_all = o.rec_reuse_all ? 1 : 0;
   p.part_o = c->part_o;
   p.part_l = c->part_l;
   p.part_o_stride = c->part_o_stride_override > 0 ? c->part_o_stride_override : elems_per_slot(c->cfg);
@@ -478,6 +576,11 @@ fb_status run_external(fb_cache* c, const void* q, const void* kp, const void* v
   if (o.to_total) {
     cp.tot_o = c->tot_o;
     cp.tot_l = c->tot_l;
+  }
+  if (o.set2 != nullptr) {
+    cp.two_sets = 1;
+    cp.splits2 = p.seg2_splits;
+    cp.base2 = p.seg2_base;
   }
   if (fused) {
     cp.out = o.out;
@@ -906,6 +1009,8 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const fb_step_opts* o
 
   fb_status st = FB_OK;
   const int groups = B * c->cfg.n_kv_heads;
+  const KeySet kept = sp ? KeySet{n_sel * fbk::kKeyTile, sp->sel, n_sel, prefix_len} : KeySet{};
+  bool sparse_done = false;   // the kept set went with the left-out set's launch
   // The step's external part: which heads recompute, and how (see each branch).
   ExtOpts eo;
   eo.kblk = k_blk;
@@ -956,13 +1061,24 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const fb_step_opts* o
     ro.follow_rec = eo.follow_rec;
     ro.cum_m = eo.cum_m;   // the sums follow the decisions this combine selects by
     if (gamma_like || dev_m || active > 0) {
-      st = run_external(c, q_blk, k_prefix, v_prefix, cached, ext_sel, ext_active, s, ro);
+      // one attention launch over both key sets and one combine (the left-out
+      // part into the cache, then the kept part, the block-internal part and
+      // the output), where the two sets' partials fit side by side
+      ExtOpts fo = ro;
+      fo.kblk = k_blk;
+      fo.vblk = v_blk;
+      fo.out = out;
+      fo.set2 = &kept;
+      fo.set2_done = &sparse_done;
+      st = run_external(c, q_blk, k_prefix, v_prefix, cached, ext_sel, ext_active, s, fo);
       if (st != FB_OK) return st;
-    } else {
-      // nothing recomputes: record the decisions (the kept launch records none)
-      hipError_t e = fbk::launch_record(ext_sel, reuse_now, (int)nh, c->cfg.n_q_heads, s);
-      if (e != hipSuccess) return hip_fail(e, "decision record launch");
+      if (!sparse_done) {
+        st = run_external(c, q_blk, k_prefix, v_prefix, cached, ext_sel, ext_active, s, ro);
+        if (st != FB_OK) return st;
+      }
     }
+    // otherwise nothing recomputes (known on the host): the kept launch below
+    // records the decisions
   }
   if (gamma_like) {   // similarity and the next step's decisions
     fbk::DecideParams dp{};
@@ -982,13 +1098,17 @@ fb_status step_impl(fb_cache* c, const fb_policy_args* pa, const fb_step_opts* o
     prof_end(c, s, &r);
     if (e != hipSuccess) return hip_fail(e, "decision launch");
   }
-  if (sp) {
-    const KeySet kept{n_sel * fbk::kKeyTile, sp->sel, n_sel, prefix_len};
+  if (sp && !sparse_done) {
     ExtOpts ko;
     ko.to_total = true;
     ko.kblk = k_blk;
     ko.vblk = v_blk;
     ko.out = out;
+    if (!(gamma_like || dev_m || active > 0)) {
+      ko.rec = reuse_now;
+      ko.follow_rec = false;
+      ko.rec_reuse_all = true;
+    }
     st = run_external(c, q_blk, k_prefix, v_prefix, kept, all_heads(c), groups, s, ko);
     if (st != FB_OK) return st;
   }

@@ -10,7 +10,6 @@ hipError_t launch_combine(int, const CombineParams&, hipStream_t) { return hipEr
 hipError_t launch_decide(const DecideParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_reset(const ResetParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_complement(const ComplementParams&, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_record(const HeadSel&, uint8_t*, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_attn_fin(const AttnParams&, const FinParams&, hipStream_t) { return hipErrorNoDevice; }
 bool fin_supported(int, int, const AttnParams&) { return false; }
 }  // namespace fbk
