@@ -19,14 +19,16 @@ from cached_attention_fb_amd import workload as wl
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu_sparse(inp, density, policy=None, device_counts=False, n_sel=None):
+def run_gpu_sparse(inp, density, policy=None, device_counts=False, n_sel=None, kv_splits=0, prof=None):
     """Every block of ``inp`` through fb_step_sparse; a fresh selection per
-    block (its prefix grows by the block).  Returns (GpuBlocks, selections)."""
+    block (its prefix grows by the block).  Returns (GpuBlocks, selections);
+    with a dict `prof`, fills it with the launches per profile kind."""
     w = inp.workload
     policy = policy or w.policy
     n0 = inp.k_prefix.shape[2]
     max_prefix = n0 + w.block * (len(inp.blocks) - 1)
-    cache = H.make_cache(w, max_prefix)
+    cache = H.make_cache(w, max_prefix, kv_splits=kv_splits)
+    cache.profile_enable(prof is not None)
     kp, vp = H.device_prefix(inp, max_prefix)
     q = torch.empty((w.batch, w.n_q_heads, w.block, w.head_dim), dtype=w.torch_dtype, device="cuda")
     kb = torch.empty((w.batch, w.n_kv_heads, w.block, w.head_dim), dtype=w.torch_dtype, device="cuda")
@@ -73,6 +75,8 @@ def run_gpu_sparse(inp, density, policy=None, device_counts=False, n_sel=None):
             vp[:, :, n:n + w.block].copy_(last.v)
         n += w.block
     torch.cuda.synchronize()
+    if prof is not None:
+        prof.update({k: v[0] for k, v in cache.profile_read().items()})
     cache.close()
     return res, sels
 
@@ -143,6 +147,25 @@ def test_sparse_always_is_exact_attention():
     dense = H.run_oracle(inp, policy="always")
     for s in range(3):
         H.tolerance_check(gpu[0].out[s], dense[0].out[s], "bf16", f"sparse always vs dense step {s}")
+
+
+@pytest.mark.parametrize("kv_splits", [0, 64])
+def test_sparse_recompute_launches(kv_splits):
+    """A step in which some head recomputes attends the left-out and the kept
+    tiles in one launch with one combine when both sets' chunks fit the
+    partial buffer together (here with the planner's own split counts),
+    and in two launches each where they do not (here forced: 64 of the 128
+    tiles kept, and the other 64 cut into 64 chunks that fill the buffer);
+    both agree with the oracle."""
+    w = wl.workload("dllm-8k").with_(steps=3, blocks=1)
+    inp = wl.generate(w, prefix=8192)
+    print(f"[sparse] recompute launches kv_splits={kv_splits}", flush=True)
+    prof = {}
+    gpu, sels = run_gpu_sparse(inp, 0.0, "always", n_sel=64, kv_splits=kv_splits, prof=prof)
+    ref = run_oracle_sparse(inp, sels, "always")
+    H.compare_block(gpu[0], ref[0], w.dtype, what=f"sparse always kv_splits={kv_splits}")
+    assert prof["external"] == prof["combine"] == 3, prof
+    assert prof["sparse_kept"] == prof["sparse_total"] == (0 if kv_splits == 0 else 3), prof
 
 
 @pytest.mark.parametrize("n_sel", [0, 1, 16])
