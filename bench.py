@@ -166,7 +166,27 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
         torch.cuda.synchronize()
         return time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3
 
+    def profiled(pol):
+        """One more pass like the timed one with HIP events around every
+        launch: per profile kind, (launches, ms)."""
+        for c in caches:
+            c.profile_enable(True)
+        state["s"] = 0
+        for _ in range(steps):
+            step(pol)
+        torch.cuda.synchronize()
+        prof = {}
+        for c in caches:
+            for kname, (cnt, tms) in c.profile_read().items():
+                a, b = prof.get(kname, (0, 0.0))
+                prof[kname] = (a + cnt, b + tms)
+            c.profile_enable(False)
+        return prof
+
     wall, gpu_s = timed(policy)
+    # the timed region's own recompute launches, in its own mix of steps (a
+    # repeat of it, profiled): the roofline's launch duration
+    prof_pol = profiled(policy)
     _, gpu_always = timed(fb.POLICY_ALWAYS)
 
     reuse_counts = []
@@ -215,20 +235,19 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
         step_stats = {"full": pct(full), "all_reuse": pct(reuse), "always": pct(always)}
 
     # profiled pass under ALWAYS: every step launches the external kernel
-    for c in caches:
-        c.profile_enable(True)
-    state["s"] = 0
-    for _ in range(steps):
-        step(fb.POLICY_ALWAYS)
-    torch.cuda.synchronize()
-    prof = {}
-    for c in caches:
-        for kname, (cnt, tms) in c.profile_read().items():
-            a, b = prof.get(kname, (0, 0.0))
-            prof[kname] = (a + cnt, b + tms)
-        c.profile_enable(False)
-    ext_us = 1e3 * prof["external"][1] / max(1, prof["external"][0])
+    # (sustained recompute: the chip runs hotter and clocks lower than in the
+    # policy's mix)
+    prof = profiled(fb.POLICY_ALWAYS)
+    ext_us_always = 1e3 * prof["external"][1] / max(1, prof["external"][0])
     kernel_us = {k: round(1e3 * v[1] / v[0], 3) for k, v in prof.items() if v[0]}
+    kernel_us_pol = {k: round(1e3 * v[1] / v[0], 3) for k, v in prof_pol.items() if v[0]}
+    # The policy pass's launches are whole recompute launches (the algorithmic
+    # work per launch) when decisions are per sequence and there is one
+    # sequence; otherwise (several sequences, or per-head decisions) a launch
+    # may cover only some heads, and the always pass stands in, as it does
+    # when the policy's pass recomputes nowhere.
+    whole = w.batch == 1 and policy_name in ("tau", "tau_cum", "always") and "external" in kernel_us_pol
+    ext_us = kernel_us_pol["external"] if whole else ext_us_always
     for c in caches:
         c.close()
     del prepared, caches, prefixes, kp0, vp0, qs, ks, vs, outs
@@ -239,14 +258,19 @@ def measure(name, steps, warmup, policy_name=None, layers=0, splits=0, decisions
     roof["kernel"] = ("attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel") + \
         " (recompute step: block-external split-KV partials + block-internal items)"
     roof["avg_launch_us"] = round(ext_us, 3)
+    roof["launches"] = prof_pol["external"][0] if whole else prof["external"][0]
+    roof["pass"] = policy_name if whole else "always"
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["algorithmic_flops_per_launch"] = alg_flops
+    roof_always = roofline(w, ext_us_always, alg_bytes, alg_flops)
+    roof_always["avg_launch_us"] = round(ext_us_always, 3)
     return {
         "w": w, "layers": layers, "kv_bytes": kv_bytes, "gpu_s": gpu_s, "wall_s": wall,
         "per_layer_step_us": 1e6 * gpu_s / steps / layers,
         "always_layer_step_us": 1e6 * gpu_always / steps / layers,
         "eff_gbs": kv_bytes * layers * steps / gpu_s / 1e9, "reuse_counts": reuse_counts,
-        "kernel_us": kernel_us, "roofline": roof, "policy": policy_name, "step_stats": step_stats,
+        "kernel_us": kernel_us, "kernel_us_policy": kernel_us_pol, "roofline": roof,
+        "roofline_always": roof_always, "policy": policy_name, "step_stats": step_stats,
     }
 
 
@@ -616,11 +640,14 @@ def sweep(prefixes=SWEEP_PREFIXES, n_blocks=3):
             "rows": rows}
 
 
-def always_only(name, steps, warmup):
-    """Recompute-every-step passes of a workload (every head recomputes at
-    every step), for profiler runs whose kernel averages must cover full
-    recompute launches only: `warmup` untimed steps, then `steps` timed ones
-    over the same layer stack as the benchmark."""
+def always_only(name, steps, warmup, policy_name="always"):
+    """Passes of one policy over a workload's block, for profiler runs: under
+    ALWAYS every head recomputes at every step, so every dispatch of the
+    attention kernel is a full recompute launch; under the workload's own
+    policy (`policy_name` "policy") they are the recompute launches of the
+    benchmark's timed region, in its own mix of steps.  `warmup` untimed
+    steps, then `steps` timed ones over the same layer stack as the
+    benchmark."""
     import torch
     from cached_attention_fb_amd import fb
     from cached_attention_fb_amd import workload as wl
@@ -639,11 +666,15 @@ def always_only(name, steps, warmup):
     qs = [st.q.cuda() for st in blk.steps]
     ks = [st.k.cuda() for st in blk.steps]
     vs = [st.v.cuda() for st in blk.steps]
-    del inp, blk
     outs = [torch.empty_like(qs[0]) for _ in range(layers)]
+    ms = [np.ascontiguousarray(st.n_updated, dtype=np.int32) for st in blk.steps]
+    del inp, blk
     prepared = [[c.prepare(qs[s], ks[s], vs[s], prefixes[li][0], prefixes[li][1], outs[li]) for s in range(S)]
                 for li, c in enumerate(caches)]
     stream = torch.cuda.current_stream().cuda_stream
+    pname = w.policy if policy_name == "policy" else policy_name
+    pol = {"tau": fb.POLICY_TAU, "gamma": fb.POLICY_GAMMA, "always": fb.POLICY_ALWAYS,
+           "tau_cum": fb.POLICY_TAU_CUM, "gamma_group": fb.POLICY_GAMMA_GROUP}[pname]
 
     def run(count):
         for i in range(count):
@@ -651,7 +682,7 @@ def always_only(name, steps, warmup):
             for li, c in enumerate(caches):
                 if s == 0:
                     c.reset(stream)
-                prepared[li][s](fb.POLICY_ALWAYS, n, None, 0, 0.0, stream)
+                prepared[li][s](pol, n, ms[s], w.tau, w.gamma, stream)
 
     run(warmup)
     torch.cuda.synchronize()
@@ -663,7 +694,7 @@ def always_only(name, steps, warmup):
     us = 1e3 * e0.elapsed_time(e1) / (steps * layers)
     for c in caches:
         c.close()
-    return {"always_only": name, "layers": layers, "steps": steps, "us_per_layer_step": round(us, 3)}
+    return {"profiled_pass": name, "policy": pname, "layers": layers, "steps": steps, "us_per_layer_step": round(us, 3)}
 
 
 def calibrate():
@@ -699,6 +730,9 @@ def main():
                     help="only run device-side threshold decisions, eager and as HIP graphs")
     ap.add_argument("--always-only", action="store_true",
                     help="only time recompute-every-step passes of --workload (profiling runs)")
+    ap.add_argument("--policy-only", action="store_true",
+                    help="only time passes of --workload under its own policy, as in the timed region "
+                         "(profiling runs)")
     args = ap.parse_args()
     if args.calibrate:
         calibrate()
@@ -720,8 +754,9 @@ def main():
     if args.sparse:
         print(json.dumps(sparse_bench(args.workload)), flush=True)
         return
-    if args.always_only:
-        print(json.dumps(always_only(args.workload, args.steps, args.warmup)), flush=True)
+    if args.always_only or args.policy_only:
+        print(json.dumps(always_only(args.workload, args.steps, args.warmup,
+                                     "always" if args.always_only else "policy")), flush=True)
         return
 
     # the largest prefix one layer's K/V can take in the free device memory
@@ -760,7 +795,11 @@ def main():
         "capacity_prefix_tokens_per_layer": capacity,
         "wall_s": round(r["wall_s"], 4),
         "kernel_avg_us_always": r["kernel_us"],
+        "kernel_avg_us_policy": r["kernel_us_policy"],
         "roofline": roof,
+        # the same kernel in the always-recompute pass (every step a recompute
+        # launch: sustained load, lower clocks)
+        "roofline_always": {**r["roofline_always"], "traffic": roof["traffic"]},
     }
     if not args.no_extra:
         extra = {}
@@ -777,7 +816,8 @@ def main():
                            "reuse_vs_full_speedup": round(e["always_layer_step_us"] / e["per_layer_step_us"], 3),
                            "effective_kv_gbs": round(e["eff_gbs"], 1),
                            "external": {**{k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac",
-                                                              "avg_launch_us")},
+                                                              "avg_launch_us", "pass")},
+                                        "frac_always": e["roofline_always"]["frac"],
                                         "traffic": None if rc is None else rc.get("hbm_bytes_per_launch"),
                                         "mfma_busy_frac": None if rc is None else rc.get("mfma_busy_frac")},
                            "kernel_avg_us_always": e["kernel_us"]}
