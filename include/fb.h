@@ -256,6 +256,12 @@ fb_status fb_step_ex(fb_cache* c, const fb_policy_args* p, const fb_step_opts* o
  *   n_sel      0 <= n_sel <= ceil(prefix_len / 64), the same for every step of
  *              a block.
  *   opts       NULL, or as for fb_step_ex (device counts).
+ * Launches: where some head recomputes, one attention launch over the
+ * left-out tiles (recomputing heads), the kept tiles (every head) and the
+ * block, and one combine, when both tile sets' split partials fit the
+ * cache's partial buffer together (else an attention launch and a combine
+ * for each set); where every head reuses (known on the host), one launch
+ * over the kept tiles and the block and one combine.
  * Under GAMMA the similarity is that of the cached (left-out) part.  The
  * cache fields A_out/L_out hold the left-out keys' part.  Policies, counts,
  * graph capture and asynchrony are as for fb_step; a block is either dense
