@@ -135,24 +135,17 @@ __device__ __forceinline__ void k_read_both(u32x4 (&r0)[D / 16], u32x4 (&r1)[D /
 }
 
 
-// P = exp2(c*s - mref) of one S^T half, the bf16 B operands of its two
-// k-steps (registers j = 8kl .. 8kl+7), and its contribution to the lane's
-// row sum: the sum of the bf16 values the PV product multiplies (so that the
-// normalised A is an exact weighted mean of V's rows under those weights),
-// two per bf16 dot-product instruction instead of one per fp32 add.
+// P = exp2(c*s - mref) of one S^T half, its contribution to the lane's row
+// sum, and the bf16 B operands of its two k-steps (registers j = 8kl .. 8kl+7).
 __device__ __forceinline__ void exp_half(f32x16& s, float mref, float c, float& lsum, bf16x8 (&pb)[2]) {
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four short sum chains instead of one long one
 #pragma unroll
-  for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (bf16)fast_exp2(fmaf(s[j], c, -mref));
-  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-  float part[2] = {0.0f, 0.0f};   // two short chains
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const bf16x8& h = pb[k >> 2];
-    const bf16x2 pr = {h[2 * (k & 3)], h[2 * (k & 3) + 1]};
-    part[k & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, part[k & 1], false);
+  for (int j = 0; j < 16; ++j) {
+    const float e = fast_exp2(fmaf(s[j], c, -mref));
+    part[j & 3] += e;
+    pb[j >> 3][j & 7] = (bf16)e;
   }
-  lsum += part[0] + part[1];
+  lsum += (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // O^T += V^T P^T for one 32-key half: k-step kl takes keys 16kl + 8(i/4) +
