@@ -691,8 +691,7 @@ bool fin_supported(int dtype, int head_dim, const AttnParams& p) {
 }
 
 hipError_t launch_attn_fin(const AttnParams& p, const FinParams& f, hipStream_t s) {
-  if (!fin_supported(FB_BF16, 128, p) || f.cp.splits > 32 || f.row_tiles != p.row_tiles ||
-      f.cp.dyn.groups != p.dyn.groups)
+  if (!fin_supported(FB_BF16, 128, p) || f.row_tiles != p.row_tiles || f.cp.dyn.groups != p.dyn.groups)
     return hipErrorNotSupported;
   if (p.waves == 8 && p.ksplit == 1) return launch_fin_batch<128, 8, 1>(p, f, s);
   if (p.waves == 8 && p.ksplit == 2) return launch_fin_batch<128, 4, 2>(p, f, s);

@@ -85,6 +85,22 @@ def test_single_launch_equals_two_launches(name, prefix, policy, monkeypatch):
         same_step(x, y, f"step {s}")
 
 
+def test_single_launch_many_splits(monkeypatch):
+    """Two kv heads over a 64k-token prefix: each group's keys go to more
+    than 32 ranges (the planner fills the chip with two groups), which the
+    combine folds in several rounds; the single launch still matches the two
+    launches."""
+    w = wl.workload("dllm-8k").with_(n_q_heads=8, n_kv_heads=2, blocks=1, steps=3)
+    inp = wl.generate(w, prefix=65536)
+    print("[single launch] 8/2 heads, prefix 65536", flush=True)
+    a, pa, ea = run(inp, "always", True, monkeypatch)
+    b, pb, eb = run(inp, "always", False, monkeypatch)
+    assert ea == 0 and eb == 0
+    assert pa["combine"] == 0 and pb["combine"] == pb["external"] == 3, (pa, pb)
+    for s, (x, y) in enumerate(zip(a, b)):
+        same_step(x, y, f"step {s}")
+
+
 def test_single_launch_graph_replays(monkeypatch):
     """A recompute step captured in a HIP graph and replayed several times with
     eager work between the replays: every replay equals the eager step (the
