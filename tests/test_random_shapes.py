@@ -90,14 +90,19 @@ def test_random_shape_device_counts(i):
 @pytest.mark.parametrize("i", [i for i in range(1, N_CASES, 2) if i % 8 != 7])
 def test_random_shape_sparse(i):
     """The bf16 shapes through fb_step_sparse with a seeded selection of
-    20-60 % of the prefix tiles (tile-list attention in every launch shape)."""
+    20-60 % of the prefix tiles (tile-list attention in every launch shape),
+    with the draw's split count (automatic or forced: the two tile sets of a
+    recompute step planned together, or the kept set cut to the left-out
+    set's range length) and, for every other case, the threshold counts in
+    device memory (the split plan chosen on the device)."""
     from test_sparse_parity import run_gpu_sparse, run_oracle_sparse
-    w, prefix, _ = draw(i)
+    w, prefix, splits = draw(i)
     density = 0.2 + 0.4 * ((i * 37) % 11) / 10
+    dev = i % 4 == 3
     print(f"[random-sparse {i}] B={w.batch} Hq/Hkv={w.n_q_heads}/{w.n_kv_heads} D={w.head_dim} "
-          f"Bs={w.block} prefix={prefix} density={density:.2f}", flush=True)
+          f"Bs={w.block} prefix={prefix} density={density:.2f} splits={splits} device_counts={dev}", flush=True)
     inp = wl.generate(w, prefix=prefix)
-    gpu, sels = run_gpu_sparse(inp, density)
+    gpu, sels = run_gpu_sparse(inp, density, device_counts=dev, kv_splits=splits)
     ref = run_oracle_sparse(inp, sels)
     for b, (g, r) in enumerate(zip(gpu, ref)):
         H.compare_block(g, r, w.dtype, what=f"random-sparse {i} block {b}")
