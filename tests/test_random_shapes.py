@@ -106,3 +106,23 @@ def test_random_shape_sparse(i):
     ref = run_oracle_sparse(inp, sels)
     for b, (g, r) in enumerate(zip(gpu, ref)):
         H.compare_block(g, r, w.dtype, what=f"random-sparse {i} block {b}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(0, N_CASES, 4))
+def test_random_shape_single_launch(i, monkeypatch):
+    """The same shapes with the opt-in single-launch step (FB_FIN=1 at cache
+    allocation), with host decisions and, for every other case, device-made
+    ones: where the kernels allow it a recompute step is one launch, else it
+    keeps the two; either way the oracle's results."""
+    w, prefix, splits = draw(i)
+    dev = i % 8 == 4
+    print(f"[random-fin {i}] {w.dtype} B={w.batch} Hq/Hkv={w.n_q_heads}/{w.n_kv_heads} D={w.head_dim} "
+          f"Bs={w.block} prefix={prefix} splits={splits} device_counts={dev}", flush=True)
+    inp = wl.generate(w, prefix=prefix)
+    monkeypatch.setenv("FB_FIN", "1")
+    gpu = H.run_gpu(inp, kv_splits=splits, device_counts=dev)
+    monkeypatch.delenv("FB_FIN", raising=False)
+    ref = H.run_oracle(inp)
+    for b, (g, r) in enumerate(zip(gpu, ref)):
+        H.compare_block(g, r, w.dtype, what=f"random-fin {i} block {b}")
