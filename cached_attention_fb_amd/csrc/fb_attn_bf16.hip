@@ -553,8 +553,9 @@ __global__ __launch_bounds__(64 * ROWW * KSPLIT) void attn_fin_kernel(const Attn
       return;
     }
     if (it.ok) attn_body<D, ROWW, KSPLIT, kModePartial, false, false, AUX, false, true>(p, it);
-    // static plan: a group without a selected head still counts its items;
-    // device plan: the items past the active groups' belong to no group
+    // static plan: every item of a selected group counts (and, without
+    // merge_reused, those of the other groups too); device plan: the items
+    // past the active groups' belong to no group
     if (it.ok || p.dyn.groups == 0) fin_arrive(f, it.b * p.hkv + it.g);
   } else {
     fin_combine<D, ROWW * KSPLIT, BATCH>(f, blockIdx.x - f.n_attn);
