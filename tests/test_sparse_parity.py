@@ -149,6 +149,18 @@ def test_sparse_always_is_exact_attention():
         H.tolerance_check(gpu[0].out[s], dense[0].out[s], "bf16", f"sparse always vs dense step {s}")
 
 
+@pytest.mark.parametrize("name,density,steps", [("dllm-8k", 0.3, None), ("long-32k-b4", 0.2, 4)])
+def test_sparse_full_size(name, density, steps):
+    """The bench's sparse configurations at their full prefix (8192 and 32768
+    tokens) under the workload's threshold: recompute steps take both tile
+    sets in one launch (one sequence, or four deciding on their own counts),
+    reuse steps the kept set alone."""
+    w = wl.workload(name).with_(blocks=1)
+    if steps:
+        w = w.with_(steps=steps)
+    _check(w, None, density)
+
+
 @pytest.mark.parametrize("kv_splits", [0, 64])
 def test_sparse_recompute_launches(kv_splits):
     """A step in which some head recomputes attends the left-out and the kept
