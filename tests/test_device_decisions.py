@@ -33,6 +33,7 @@ def _workload(name):
     ("tiny-fp32", None, "tau_cum"),
     ("dllm-8k", 1000, "tau"),
     ("dllm-8k", 1000, "tau_cum"),
+    ("dllm-8k", None, "tau"),         # the full 8192-token prefix
     ("long-32k-b4", 700, "tau"),      # four sequences, each deciding on its own count
 ])
 def test_device_counts_match_host_and_oracle(name, prefix, policy):
